@@ -1,0 +1,268 @@
+"""Oracle pins for the one-sided path: Hessian, factorization, column loop.
+
+Each check ties the oracle to something other than itself: brute force, a
+textbook algorithm computed another way (Gram-Schmidt nearest plane), closed
+forms and exact invariants of the method.  CPU only.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import gptq_oracle as go
+from post_weight_quantization_syrk_amd import synth
+
+
+def _spd(d, seed, corr=0.5, n=None):
+    """A correlated SPD Hessian 2 X^T X from a small random X."""
+    rng = np.random.default_rng(seed)
+    n = n or 4 * d
+    base = rng.standard_normal((n, d))
+    mix = np.eye(d) + corr * rng.standard_normal((d, d)) / np.sqrt(d)
+    x = base @ mix * np.exp(0.5 * rng.standard_normal(d))
+    return 2.0 * x.T @ x, x
+
+
+# ---------------------------------------------------------------- Hessian
+def test_hessian_bruteforce():
+    rng = np.random.default_rng(0)
+    x = rng.integers(-3, 4, size=(7, 4)).astype(np.float64)
+    H = oracle.hessian([x[:3], x[3:]])
+    for i in range(4):
+        for j in range(4):
+            s = 0.0
+            for t in range(7):
+                s += x[t, i] * x[t, j]
+            assert H[i, j] == 2 * s
+            assert oracle.hessian_entry(x, i, j) == 2 * s
+
+
+def test_hessian_bf16_widening_is_exact():
+    wl = synth.scaled(synth.ATTN7B, d_in=64, n_tokens=256)
+    xb = synth.x_chunk(wl, 0)
+    x64 = synth.as_f64(xb, "bf16")
+    # bf16 has 8 significant bits: every widened value is an exact multiple of
+    # its exponent's 2^-7 step, and re-rounding to bf16 gives the same bits.
+    np.testing.assert_array_equal(synth.f32_to_bf16_bits(x64.astype(np.float32)), xb)
+
+
+# ------------------------------------------------------- factorization
+@pytest.mark.parametrize("d", [1, 5, 64, 300])
+def test_cholesky_and_upper_factor(d):
+    H0, _ = _spd(d, d)
+    p = oracle.prepare(H0, damp=0.01)
+    H, L, U = p["H"], p["L"], p["U"]
+    assert np.linalg.norm(L @ L.T - H) / np.linalg.norm(H) <= 1e-13
+    assert np.allclose(np.tril(L), L) and np.allclose(np.triu(U), U)
+    assert np.all(np.diag(U) > 0)
+    err = np.linalg.norm(U.T @ U @ H - np.eye(d)) / np.sqrt(d)
+    assert err <= 1e-10
+    # damping is relative: lambda = 0.01 * mean(diag) of the undamped matrix
+    assert p["lam"] == pytest.approx(0.01 * np.mean(np.diag(H0)), rel=1e-15)
+    np.testing.assert_allclose(np.diag(H) - np.diag(H0), p["lam"], rtol=1e-12)
+
+
+def test_literal_route_equals_reversed_route():
+    H0, _ = _spd(80, 3)
+    p = oracle.prepare(H0)
+    U2 = oracle.reversed_route_U(p["H"])
+    assert np.max(np.abs(U2 - p["U"])) / np.max(np.abs(p["U"])) < 1e-11
+
+
+def test_dead_channels():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((50, 6))
+    x[:, 2] = 0.0
+    H0 = oracle.hessian([x])
+    p = oracle.prepare(H0, damp=0.01)
+    assert p["dead"].tolist() == [False, False, True, False, False, False]
+    # dead diagonal set to 1 before the mean is taken
+    d = np.diag(H0).copy()
+    d[2] = 1.0
+    assert p["lam"] == pytest.approx(0.01 * d.mean(), rel=1e-15)
+    W = rng.standard_normal((3, 6))
+    r = oracle.gptq(W, p["U"], p["dead"], bits=4, group_size=-1)
+    # the dead column is rounded as zero and does not change the loss
+    assert np.all(r["What"][:, 2] == 0.0)
+
+
+def test_not_spd():
+    with pytest.raises(oracle.NotSPD) as e:
+        oracle.prepare(-np.eye(4), damp=0.01)
+    assert e.value.pivot == 1
+    with pytest.raises(oracle.NotSPD) as e:
+        oracle.prepare(np.array([[1.0, 2.0], [2.0, 1.0]]), damp=0.0)
+    assert e.value.pivot == 2
+    # an all-zero H is all dead channels: it becomes the identity
+    p = oracle.prepare(np.zeros((3, 3)), damp=0.01)
+    np.testing.assert_allclose(p["H"], 1.01 * np.eye(3))
+
+
+def test_nonfinite_rejected():
+    H = np.eye(3)
+    H[1, 1] = np.nan
+    with pytest.raises(ValueError):
+        oracle.prepare(H)
+    with pytest.raises(ValueError):
+        oracle.hessian([np.array([[np.inf, 1.0]])])
+
+
+# ------------------------------------------------------- column loop
+QUANT_CASES = [(4, 128, False), (4, 64, True), (3, 64, True), (3, 32, False),
+               (2, 32, False), (4, -1, False), (2, -1, True)]
+
+
+@pytest.mark.parametrize("bits,g,sym", QUANT_CASES)
+def test_identity_hessian_is_rtn_bit_for_bit(bits, g, sym):
+    rng = np.random.default_rng(bits * 100 + abs(g) + sym)
+    W = 0.02 * rng.standard_normal((17, 256))
+    W[3, 7] = 0.6  # an outlier
+    p = oracle.prepare(2.0 * np.eye(256), damp=0.01)
+    for block in (None, 128):
+        r = oracle.gptq(W, p["U"], p["dead"], bits=bits, group_size=g, sym=sym, block=block)
+        ref = oracle.rtn(W, bits=bits, group_size=g, sym=sym)
+        np.testing.assert_array_equal(r["codes"], ref["codes"])
+        np.testing.assert_array_equal(r["scales"], ref["scales"])
+        np.testing.assert_array_equal(r["zeros"], ref["zeros"])
+        np.testing.assert_array_equal(r["What"], ref["What"])
+
+
+def test_any_diagonal_hessian_is_rtn():
+    rng = np.random.default_rng(11)
+    W = 0.02 * rng.standard_normal((9, 128))
+    p = oracle.prepare(np.diag(np.exp(rng.standard_normal(128))), damp=0.0)
+    assert np.count_nonzero(np.triu(p["U"], 1)) == 0
+    r = oracle.gptq(W, p["U"], bits=3, group_size=32, sym=False)
+    np.testing.assert_array_equal(r["codes"], oracle.rtn(W, bits=3, group_size=32)["codes"])
+
+
+def _babai_gram_schmidt(w, H, scales):
+    """Textbook nearest-plane rounding of target F w^T on the lattice with basis
+    vectors b_j = s_j F e_j, where F is the symmetric square root of H (so
+    F^T F = H; no Cholesky anywhere).  The basis is ordered so that column 0
+    is the LAST vector: nearest plane fixes the last coordinate first."""
+    lam, Q = np.linalg.eigh(H)
+    F = Q @ np.diag(np.sqrt(lam)) @ Q.T
+    n = len(w)
+    order = list(range(n - 1, -1, -1))            # c_1 = b_{n-1}, ..., c_n = b_0
+    C = np.stack([scales[j] * F[:, j] for j in order], axis=1)
+    # modified Gram-Schmidt
+    Cs = C.copy()
+    for k in range(n):
+        for i in range(k):
+            Cs[:, k] -= (Cs[:, i] @ C[:, k]) / (Cs[:, i] @ Cs[:, i]) * Cs[:, i]
+    t = F @ w
+    z = np.zeros(n)
+    for k in range(n - 1, -1, -1):
+        z[k] = np.rint((t @ Cs[:, k]) / (Cs[:, k] @ Cs[:, k]))
+        t = t - z[k] * C[:, k]
+    q = np.zeros(n)
+    for k, j in enumerate(order):
+        q[j] = z[k]
+    return q
+
+
+@pytest.mark.parametrize("d_in,seed", [(4, 0), (7, 1), (9, 2), (12, 3), (12, 4)])
+def test_feedback_equals_babai_nearest_plane(d_in, seed):
+    rng = np.random.default_rng(100 + seed)
+    H, _ = _spd(d_in, 200 + seed, corr=1.5)
+    p = oracle.prepare(H, damp=0.0)
+    scales = 0.05 * np.exp(0.3 * rng.standard_normal(d_in))
+    W = rng.standard_normal((4, d_in)) * 0.2
+    for block in (None, 4):
+        _, What, _ = oracle.column_loop(
+            W, p["U"], lambda j, Wc: scales[j] * np.rint(Wc[:, j] / scales[j]), block=block)
+        for r in range(W.shape[0]):
+            q = _babai_gram_schmidt(W[r], H, scales)
+            np.testing.assert_array_equal(np.rint(What[r] / scales), q)
+
+
+@pytest.mark.parametrize("bits,g,sym", QUANT_CASES[:4])
+def test_delta_identity(bits, g, sym):
+    """Per row, sum_j delta_j^2 = (w - w_hat) H (w - w_hat)^T with the damped H,
+    because e = delta U and U H U^T = I."""
+    H0, _ = _spd(128, 7, corr=1.0)
+    rng = np.random.default_rng(8)
+    W = 0.02 * rng.standard_normal((6, 128))
+    p = oracle.prepare(H0)
+    r = oracle.gptq(W, p["U"], p["dead"], bits=bits, group_size=g, sym=sym, block=128)
+    E = W - r["What"]
+    quad = np.einsum("ij,jk,ik->i", E, p["H"], E)
+    np.testing.assert_allclose(r["loss_damped"], quad, rtol=1e-10)
+
+
+def test_power_of_two_scaling_invariance():
+    H0, _ = _spd(96, 9, corr=1.0)
+    rng = np.random.default_rng(10)
+    W = 0.02 * rng.standard_normal((8, 96))
+    a = oracle.gptq(W, oracle.prepare(H0)["U"], bits=3, group_size=32)
+    b = oracle.gptq(W, oracle.prepare(4.0 * H0)["U"], bits=3, group_size=32)
+    np.testing.assert_array_equal(a["codes"], b["codes"])
+    np.testing.assert_array_equal(a["What"], b["What"])
+
+
+def test_sequential_equals_lazy_on_small_workload():
+    wl = synth.SMALL
+    x = synth.as_f64(synth.x_chunk(wl, 0), wl.x_dtype)
+    W = synth.as_f64(synth.w_matrix(wl), wl.w_dtype)
+    H0 = oracle.hessian([x])
+    p = oracle.prepare(H0, wl.damp)
+    seq = oracle.gptq(W, p["U"], p["dead"], bits=4, group_size=128, block=None)
+    lazy = oracle.gptq(W, p["U"], p["dead"], bits=4, group_size=128, block=128)
+    np.testing.assert_array_equal(seq["codes"], lazy["codes"])
+    np.testing.assert_array_equal(seq["scales"], lazy["scales"])
+    np.testing.assert_allclose(seq["What"], lazy["What"], atol=1e-15)
+    # GPTQ does what it is for on this layer: less output error than RTN
+    l_g = oracle.layer_loss(W, seq["What"], H0)
+    l_r = oracle.layer_loss(W, oracle.rtn(W, bits=4, group_size=128)["What"], H0)
+    assert l_g < l_r
+
+
+def test_layer_loss_is_output_error():
+    rng = np.random.default_rng(12)
+    x = rng.standard_normal((40, 10))
+    W = rng.standard_normal((3, 10))
+    Wh = W + 0.01 * rng.standard_normal((3, 10))
+    H0 = oracle.hessian([x])
+    out = np.sum(((W - Wh) @ x.T) ** 2)
+    assert oracle.layer_loss(W, Wh, H0) == pytest.approx(2 * out, rel=1e-12)
+
+
+# ---------------------------------------------- planted mistakes are caught
+def test_pins_catch_planted_mistakes(monkeypatch):
+    """Plant plausible slips in the oracle and check that the pins above fail."""
+    d_in = 9
+    H, _ = _spd(d_in, 201, corr=1.5)
+    rng = np.random.default_rng(101)
+    scales = 0.05 * np.exp(0.3 * rng.standard_normal(d_in))
+    W = rng.standard_normal((4, d_in)) * 0.2
+    ref = np.array([_babai_gram_schmidt(W[r], H, scales) for r in range(4)])
+
+    def run(U):
+        _, What, _ = oracle.column_loop(
+            W, U, lambda j, Wc: scales[j] * np.rint(Wc[:, j] / scales[j]))
+        return np.rint(What / scales)
+
+    U = oracle.prepare(H, damp=0.0)["U"]
+    assert np.array_equal(run(U), ref)
+    # (a) transposed operand: U^T is lower triangular, so no feedback at all
+    assert not np.array_equal(run(U.T.copy()), ref)
+    # (a') a dropped term: feedback reaches only the next column
+    U1 = np.diag(np.diag(U)) + np.diag(np.diag(U, 1), 1)
+    assert not np.array_equal(run(U1), ref)
+    # (b) factor of H instead of H^-1
+    Lh = np.linalg.cholesky(H)
+    assert not np.array_equal(run(Lh.T), ref)
+    # (c) wrong sign of the feedback
+    orig = np.outer
+    monkeypatch.setattr(go.np, "outer", lambda a, b: -orig(a, b))
+    assert not np.array_equal(run(U), ref)
+    monkeypatch.setattr(go.np, "outer", orig)
+    # (d) damping dropped from the mean: delta identity with the damped H fails
+    H0, _ = _spd(64, 7, corr=1.0)
+    Wd = 0.02 * np.random.default_rng(8).standard_normal((4, 64))
+    p = oracle.prepare(H0)
+    Uwrong = oracle.prepare(H0, damp=0.0)["U"]
+    r = oracle.gptq(Wd, Uwrong, bits=3, group_size=32)
+    E = Wd - r["What"]
+    quad = np.einsum("ij,jk,ik->i", E, p["H"], E)
+    assert not np.allclose(r["loss_damped"], quad, rtol=1e-6)
