@@ -1,0 +1,231 @@
+#!/usr/bin/env python3
+"""Throughput of GPTQ's per-layer quantization path on one MI355X.
+
+Workload: one Llama-7B-shaped attention projection, W 4096 x 4096 bf16, from
+262144 bf16 calibration tokens (128 sequences x 2048), 4-bit asymmetric,
+group size 128, block 128, damping 0.01 -- synthetic seeded inputs that stand
+in for a real model's weights and activations.
+
+One step = the whole path on resident inputs: zero H, H += 2 X^T X over all
+tokens, damping + factorization -> U, the greedy column loop with lazy
+trailing updates, and packing.  Each stage is bracketed by HIP events on the
+stream the library launches on.  Prints one JSON line on stdout; progress
+goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    p = os.path.join(ROOT, "post_weight_quantization_syrk_amd", "csrc", "syrk.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile():
+    """HBM bytes per SYRK launch from the committed PMC summary, if it was
+    taken on the current kernel source (else None)."""
+    p = os.path.join(ROOT, "profiles", "syrk_bf16_attn4096_262144tok_traffic.json")
+    try:
+        rec = json.load(open(p))
+    except (OSError, ValueError):
+        return None
+    if rec.get("syrk_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(wl, synth, max_seconds=30.0):
+    """The float64 oracle, as it stands, on a bounded sample of the workload,
+    scaled to whole-layer weights/s."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        blas_threads = None
+    cores = len(os.sched_getaffinity(0))
+    n_tok, n_rows = 4096, 256
+    sub = synth.scaled(wl, n_tokens=n_tok, chunk_tokens=n_tok)
+    x = synth.as_f64(synth.x_chunk(sub, 0), "bf16")
+    t0 = time.perf_counter()
+    H0 = oracle.hessian([x])
+    t_h = (time.perf_counter() - t0) * (wl.n_tokens / n_tok)
+    t0 = time.perf_counter()
+    p = oracle.prepare(H0, wl.damp)
+    t_p = time.perf_counter() - t0
+    W = synth.as_f64(synth.w_matrix(wl), "bf16")[:n_rows]
+    t0 = time.perf_counter()
+    r = oracle.gptq(W, p["U"], p["dead"], bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                    block=wl.block)
+    t_q = (time.perf_counter() - t0) * (wl.d_out / n_rows)
+    t0 = time.perf_counter()
+    oracle.pack_rows(r["codes"], wl.bits)
+    oracle.fp16_bits(r["scales"])
+    oracle.fp16_bits(r["zeros"])
+    t_k = (time.perf_counter() - t0) * (wl.d_out / n_rows)
+    total = t_h + t_p + t_q + t_k
+    return {
+        "value": wl.d_out * wl.d_in / total,
+        "unit": "weights/s",
+        "cores": cores,
+        "blas_threads": blas_threads,
+        "kind": "oracle",
+        "sample": (f"Hessian over {n_tok} of {wl.n_tokens} tokens (x{wl.n_tokens // n_tok}); "
+                   f"full 4096x4096 factorization; column loop and packing on {n_rows} of "
+                   f"{wl.d_out} rows (x{wl.d_out // n_rows}); float64 numpy/LAPACK, "
+                   f"elementwise numpy single-threaded"),
+        "stage_seconds_extrapolated": {"hessian": t_h, "prepare": t_p, "quantize": t_q,
+                                       "pack": t_k},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the quantization path runs on a single MI355X "
+              "here; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from post_weight_quantization_syrk_amd import gptq, synth
+
+    wl = synth.ATTN7B
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gptq.lib()
+    d_out, d_in, n = wl.d_out, wl.d_in, wl.n_tokens
+    log(f"generating inputs: X {n}x{d_in} bf16, W {d_out}x{d_in} bf16")
+    t0 = time.time()
+    xb = synth.x_full(wl)
+    X = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+    del xb
+    W = torch.from_numpy(synth.w_matrix(wl).view("int16")).to(dev).view(torch.bfloat16)
+    log(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
+
+    H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
+    U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+    dead = torch.empty(d_in, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    ng = d_in // wl.group_size
+    codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, ng), dtype=torch.float32, device=dev)
+    zeros = torch.empty((d_out, ng), dtype=torch.float32, device=dev)
+    qweight = torch.empty((d_out, d_in * wl.bits // 32), dtype=torch.int32, device=dev)
+    s16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    z16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, gptq.GPTQ_BF16), dtype=torch.uint8,
+                       device=dev)
+    ws_p = torch.empty(gptq.gptq_prepare_workspace(d_in), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(gptq.gptq_quantize_workspace(d_out, d_in, wl.block), dtype=torch.uint8,
+                       device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ["hessian", "prepare", "quantize", "pack"]
+
+    def step(ev=None):
+        H.zero_()
+        if ev: ev[0].record(stream)
+        gptq.gptq_hessian_accumulate(H, X, ws=ws_h)
+        if ev: ev[1].record(stream)
+        gptq.gptq_prepare_hinv(H, wl.damp, U, dead, status, ws=ws_p, check=False)
+        if ev: ev[2].record(stream)
+        gptq.gptq_quantize_layer(W, U, dead, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                                 block=wl.block, codes=codes, scales=scales, zeros=zeros,
+                                 want_loss=False, ws=ws_q)
+        if ev: ev[3].record(stream)
+        gptq.gptq_pack(codes, scales, zeros, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                       qweight=qweight, scales_f16=s16, zeros_f16=z16)
+        if ev: ev[4].record(stream)
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("factorization failed during warmup")
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {s: sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
+                / args.steps for i, s in enumerate(stages)}
+    if int(status.item()) != 0:
+        raise RuntimeError("factorization failed")
+    log(f"{ms_step:.3f} ms/step; stages " + ", ".join(f"{k} {v:.3f} ms" for k, v in stage_ms.items()))
+
+    weights = d_out * d_in
+    value = weights / (ms_step / 1e3)
+    syrk_flops = float(n) * d_in * (d_in + 1)
+    trail_flops = float(d_out) * d_in * (d_in - wl.block)
+    syrk_tflops = syrk_flops / (stage_ms["hessian"] / 1e3) / 1e12
+    roofline = {
+        "kernel": "syrk_bf16_kernel (H += 2 X^T X, incl. fused split-K reduction)",
+        "bound": "mfma",
+        "achieved": round(syrk_tflops, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(syrk_tflops / PEAK_BF16_TFLOPS, 4),
+        "traffic": traffic_from_profile(),
+        "algorithmic_flops_per_launch": syrk_flops,
+        "avg_launch_ms": round(stage_ms["hessian"], 4),
+    }
+    upd_tflops = (syrk_flops + trail_flops) / ((stage_ms["hessian"] + stage_ms["quantize"]) / 1e3) / 1e12
+    line = {
+        "metric": "GPTQ weights quantized/sec/GPU (4096x4096, 262144 tokens)",
+        "value": round(value, 1),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; stands in for a 7B model's weights and 128x2048 calibration tokens)",
+        "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "tokens": n,
+                   "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym,
+                   "block": wl.block, "damp": wl.damp},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "secondary": {"metric": "SYRK+update TFLOP/s", "value": round(upd_tflops, 2),
+                      "unit": "TFLOP/s",
+                      "note": "(n d(d+1) + d_out d_in (d_in-128)) / (hessian + quantize stage "
+                              "time); the quantize stage also holds the column loop"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample (cpu_baseline)")
+        line["cpu_baseline"] = cpu_baseline(wl, synth)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

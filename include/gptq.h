@@ -1,0 +1,171 @@
+/*
+ * gptq.h -- C ABI of libgptq_mi355x.so: GPTQ's per-layer quantization hot path
+ * on AMD MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [P1] "GPTQ：基于近似二阶信息的大模型权重量化"  (GPTQ tutorial)
+ *   [P4] "GPTQ: практическое квантование языковых моделей без потери смысла"
+ *   [P5] "GPTQ/AWQ量化中Group Size的精确含义与计算"  (group-size explainer)
+ *
+ * Conventions shared by every call
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, unless
+ *     marked "host".  The library allocates no memory and keeps no state
+ *     between calls; scratch space is passed in as `ws` of `ws_bytes` bytes,
+ *     sized by the matching *_workspace() query (pass ws = NULL when the
+ *     query returns 0).  `ws` must be 256-byte aligned.
+ *   - Matrices are row-major and dense unless a leading dimension is given.
+ *   - Every call only enqueues work on `stream` (a hipStream_t; NULL = the
+ *     null stream) and returns at once.  Results are valid once the stream
+ *     has been synchronised.
+ *   - Argument errors are reported synchronously, before anything is
+ *     enqueued, as GPTQ_EINVAL / GPTQ_EUNSUPPORTED; a failed launch returns
+ *     GPTQ_EHIP.  A factorization breakdown is only known on the device and
+ *     is written to `dev_status` (see gptq_prepare_hinv).
+ *   - NaN/Inf inputs are not detected; their outputs are unspecified.
+ *   - Calls that share a workspace or an output buffer must not overlap in
+ *     time (use one stream, or synchronise between them).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = 1,       /* bad pointer, size or parameter */
+  GPTQ_EUNSUPPORTED = 2, /* valid for the method but not implemented here */
+  GPTQ_EHIP = 3,         /* a HIP launch or runtime call failed */
+  GPTQ_ENOTSPD = 4       /* the damped Hessian is not positive definite */
+} gptq_status;
+
+typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
+
+/* hipStream_t, kept opaque so this header needs no HIP include. */
+typedef void* gptq_stream;
+
+/* ---------------------------------------------------------------------------
+ * Hessian accumulation.  [P1] 阶段一: the layer's Hessian is H = 2 X^T X over
+ * the calibration tokens X [n x d_in].
+ *
+ *   H += 2 * X^T X
+ *
+ * H        [d x d] float32, row-major.  Only the lower triangle (diagonal
+ *          included) is read and written; the strict upper triangle is left
+ *          untouched.  Zero it before the first call; call again on further
+ *          token chunks to accumulate (a saved H is a complete resume point).
+ * X        [n_tokens x ldx] elements of x_dtype, row-major; columns 0..d-1
+ *          are used.  bf16 values are widened exactly; products are formed
+ *          exactly in float32 and summed in float32.
+ * n_tokens >= 0 (0 is a no-op); ldx >= d; d >= 1.
+ * ws       scratch of gptq_hessian_workspace(d, n_tokens, x_dtype) bytes.
+ * The result is deterministic: the same inputs give the same bits.
+ * ------------------------------------------------------------------------- */
+int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype,
+                            int64_t n_tokens, int64_t ldx, void* ws, size_t ws_bytes,
+                            gptq_stream stream);
+size_t gptq_hessian_workspace(int64_t d, int64_t n_tokens, int x_dtype);
+
+/* ---------------------------------------------------------------------------
+ * Damping, Cholesky and the upper factor of the inverse.  [P1] 阶段一 (H ~
+ * 2X^T X + lambda I, then a Cholesky factorization whose triangular factor is
+ * used row by row instead of a full inverse).
+ *
+ * In place on H (lower triangle read):
+ *   1. dead[i] = (H_ii == 0); for dead i, H_ii = 1 (such an input channel is
+ *      always zero; its weights are then quantized as 0);
+ *   2. H += lambda I with lambda = damp * mean(diag H)   (damp = 0.01 usual);
+ *   3. the strict upper triangle is overwritten with the mirror of the lower.
+ * Then U [d x d] float32 is written: the upper triangular matrix with positive
+ * diagonal and U^T U = H^{-1} (the strict lower triangle of U is set to 0).
+ * It is computed as U = V^{-1} where H = V V^T with V upper triangular, which
+ * is the same unique factor as chol(H^{-1}); arithmetic is float64.
+ *
+ * dead       [d] uint8 out, may be NULL.
+ * dev_status [1] int32 out (device): 0 on success, otherwise 1 + the index
+ *            (in H's numbering) of the first diagonal element found
+ *            non-positive.  The elimination runs from index d-1 down to 0.
+ *            U is unspecified when dev_status != 0.
+ * ws         scratch of gptq_prepare_workspace(d) bytes.
+ * ------------------------------------------------------------------------- */
+int gptq_prepare_hinv(float* H, int64_t d, double damp, float* U, uint8_t* dead,
+                      int32_t* dev_status, void* ws, size_t ws_bytes, gptq_stream stream);
+size_t gptq_prepare_workspace(int64_t d);
+
+/* ---------------------------------------------------------------------------
+ * Greedy column-by-column quantization with error feedback.  [P1] 阶段二
+ * (fixed ascending column order, lazy batched updates), 对称与仿射量化
+ * (q = round(x/s) + z), 量化误差与补偿; [P4] rows are independent; [P5] group
+ * sizes, the 0..2^b-1 grid and the zero point.
+ *
+ * For each row independently, columns j = 0..d_in-1 in order:
+ *   at a group's first column (every group_size columns; only column 0 when
+ *   group_size = -1, the whole row being one group) the group's CURRENT
+ *   values v (after all feedback so far) give
+ *     asymmetric: lo = min(0, min v), hi = max(0, max v),
+ *                 scale = fp16((hi - lo)/maxq), zero = clamp(round(-lo/scale), 0, maxq)
+ *     symmetric:  scale = fp16(2 max|v| / maxq), zero = (maxq + 1)/2
+ *     (fp16 = one rounding of the float64 quotient to binary16, nearest-even;
+ *      a zero range, or a scale that rounds to 0, gives scale = 1)
+ *   q_j = clamp(round(w_j/scale) + zero, 0, maxq)   (round: nearest integer
+ *         of the exact quotient, ties to even);  w_hat_j = scale (q_j - zero)
+ *   delta_j = (w_j - w_hat_j) / U_jj;  w_k -= delta_j U_jk for all k > j.
+ * The feedback to columns past the current block of `block` columns is
+ * applied once per block as one matrix product (lazy batching); in exact
+ * arithmetic this equals the column-by-column form.
+ *
+ * W        [d_out x d_in] of w_dtype (bf16 or float32), read only.
+ * U        [d_in x d_in] float32 from gptq_prepare_hinv (upper triangle read).
+ * dead     [d_in] uint8 or NULL; columns with dead[i] != 0 are zeroed first.
+ * bits     2, 3 or 4 (maxq = 2^bits - 1).
+ * group_size  32, 64, 128, or -1 (one group per row).  Must divide d_in.
+ * sym      0 asymmetric, 1 symmetric.
+ * block    128 (the only supported value).
+ * codes    [d_out x d_in] uint8 out.
+ * scales   [d_out x n_groups] float32 out (values exact in binary16);
+ *          n_groups = d_in / group_size, or 1 when group_size = -1.
+ * zeros    [d_out x n_groups] float32 out (integers).
+ * loss_rows [d_out] float32 out or NULL: sum_j delta_j^2 per row, which
+ *          equals (w - w_hat) H (w - w_hat)^T for the damped H.
+ * ws       scratch of gptq_quantize_workspace(d_out, d_in, block) bytes.
+ * d_out may be 0 (no-op).
+ * ------------------------------------------------------------------------- */
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                        const float* U, const uint8_t* dead, int bits, int group_size,
+                        int sym, int block, uint8_t* codes, float* scales, float* zeros,
+                        float* loss_rows, void* ws, size_t ws_bytes, gptq_stream stream);
+size_t gptq_quantize_workspace(int64_t d_out, int64_t d_in, int block);
+
+/* ---------------------------------------------------------------------------
+ * Packing.  [P5] 存储代价 gives the bit budget (b-bit codes, 16-bit scale and
+ * a zero point per group; no zero when symmetric) but no layout; the layout
+ * here is: the codes of a row form a little-endian bit stream, code j in bits
+ * [b*j, b*j + b), cut into uint32 words, ceil(d_in*b/32) words per row
+ * (3-bit codes straddle words: 32 codes per 3 words).
+ *
+ * codes      [d_out x d_in] uint8, each < 2^bits.
+ * scales     [d_out x n_groups] float32 (binary16-exact), zeros likewise.
+ * qweight    [d_out x ceil(d_in*bits/32)] uint32 out.
+ * scales_f16 [d_out x n_groups] uint16 out: IEEE binary16 bits of scales.
+ * zeros_f16  [d_out x n_groups] uint16 out: binary16 bits of zeros; not
+ *            written when sym != 0 (may then be NULL).
+ * ------------------------------------------------------------------------- */
+int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int64_t d_out,
+              int64_t d_in, int bits, int group_size, int sym, uint32_t* qweight,
+              uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream);
+
+/* Host: static description of a status code. */
+const char* gptq_strerror(int status);
+
+/* Host: ABI version (major * 100 + minor). */
+int gptq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GPTQ_MI355X_H */

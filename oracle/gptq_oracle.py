@@ -157,8 +157,13 @@ def reversed_route_U(H: np.ndarray) -> np.ndarray:
 # ---------------------------------------------------------------------------
 # 6. Quantizer: group parameters and rounding
 # ---------------------------------------------------------------------------
-def group_params(v: np.ndarray, bits: int, sym: bool):
-    """Scale (binary16 value) and integer zero of each row of ``v`` [rows, G]."""
+def group_params(v: np.ndarray, bits: int, sym: bool, with_raw: bool = False):
+    """Scale (binary16 value) and integer zero of each row of ``v`` [rows, G].
+
+    With ``with_raw`` also returns the unrounded step (hi-lo)/maxq or
+    2 max|v|/maxq and the unrounded zero -lo/scale, for reporting how close a
+    value sat to a rounding boundary.
+    """
     maxq = maxq_for(bits)
     v = np.asarray(v, dtype=np.float64)
     rows = v.shape[0]
@@ -170,6 +175,8 @@ def group_params(v: np.ndarray, bits: int, sym: bool):
         s16 = fp16_rne(raw)
         ok = (amax > 0) & (s16 > 0)
         scale[ok] = s16[ok]
+        if with_raw:
+            return scale, zero, raw, zero.copy()
         return scale, zero
     lo = np.minimum(0.0, np.min(v, axis=1)) if v.shape[1] else np.zeros(rows)
     hi = np.maximum(0.0, np.max(v, axis=1)) if v.shape[1] else np.zeros(rows)
@@ -178,7 +185,10 @@ def group_params(v: np.ndarray, bits: int, sym: bool):
     ok = (hi > lo) & (s16 > 0)
     scale[ok] = s16[ok]
     zero = np.zeros(rows)
-    zero[ok] = np.clip(np.rint(-lo[ok] / scale[ok]), 0, maxq)
+    zraw = -lo / scale
+    zero[ok] = np.clip(np.rint(zraw[ok]), 0, maxq)
+    if with_raw:
+        return scale, zero, raw, zraw
     return scale, zero
 
 
@@ -242,22 +252,29 @@ def gptq(W, U, dead=None, *, bits=4, group_size=128, sym=False, block=None):
     ng = d_in // G
     scales = np.zeros((d_out, ng))
     zeros = np.zeros((d_out, ng))
+    raw_scales = np.zeros((d_out, ng))
+    raw_zeros = np.zeros((d_out, ng))
+    raw_q = np.zeros((d_out, d_in))
     codes = np.zeros((d_out, d_in), dtype=np.uint8)
     cur = {}
 
     def qcol(j, Wc):
         if j % G == 0:
-            s, z = group_params(Wc[:, j:j + G], bits, sym)
+            s, z, rs, rz = group_params(Wc[:, j:j + G], bits, sym, with_raw=True)
             scales[:, j // G] = s
             zeros[:, j // G] = z
+            raw_scales[:, j // G] = rs
+            raw_zeros[:, j // G] = rz
             cur["s"], cur["z"] = s, z
         q, wh = quantize_values(Wc[:, j], cur["s"], cur["z"], maxq)
         codes[:, j] = q.astype(np.uint8)
+        raw_q[:, j] = Wc[:, j] / cur["s"]
         return wh
 
     _, What, delta = column_loop(W, U, qcol, block=block)
     return dict(codes=codes, scales=scales, zeros=zeros, What=What, delta=delta,
-                loss_damped=np.sum(delta * delta, axis=1))
+                loss_damped=np.sum(delta * delta, axis=1), raw_scales=raw_scales,
+                raw_zeros=raw_zeros, raw_q=raw_q)
 
 
 def rtn(W, *, bits=4, group_size=128, sym=False):

@@ -1,0 +1,113 @@
+// C ABI front end: argument checks, workspace sizing and launch sequencing.
+// Every entry point validates its arguments before enqueueing anything.
+#include <hip/hip_runtime.h>
+
+#include "../../include/gptq.h"
+#include "kernels.h"
+
+namespace {
+
+inline bool aligned256(const void* p) { return ((uintptr_t)p & 255u) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? GPTQ_OK : GPTQ_EHIP; }
+
+bool valid_group(int64_t d_in, int group_size) {
+  if (group_size == -1) return true;
+  return group_size > 0 && d_in % group_size == 0;
+}
+
+bool supported_group(int group_size) {
+  return group_size == -1 || group_size == 32 || group_size == 64 || group_size == 128;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gptq_abi_version(void) { return 100; }
+
+const char* gptq_strerror(int status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_EUNSUPPORTED: return "unsupported parameter";
+    case GPTQ_EHIP: return "HIP runtime or launch failure";
+    case GPTQ_ENOTSPD: return "Hessian not positive definite";
+    default: return "unknown status";
+  }
+}
+
+size_t gptq_hessian_workspace(int64_t d, int64_t n_tokens, int x_dtype) {
+  if (d <= 0 || n_tokens < 0 || (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32)) return 0;
+  if (n_tokens == 0) return 0;
+  return gptq::syrk_plan(d, n_tokens, x_dtype).ws_bytes;
+}
+
+int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int64_t n_tokens,
+                            int64_t ldx, void* ws, size_t ws_bytes, gptq_stream stream) {
+  if (d <= 0 || d > (int64_t)1 << 20 || n_tokens < 0 || ldx < d) return GPTQ_EINVAL;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (!H) return GPTQ_EINVAL;
+  if (n_tokens == 0) return GPTQ_OK;
+  if (!X) return GPTQ_EINVAL;
+  const gptq::SyrkPlan plan = gptq::syrk_plan(d, n_tokens, x_dtype);
+  if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && (!ws || !aligned256(ws)))) return GPTQ_EINVAL;
+  return hip_status(
+      gptq::syrk_launch(H, d, X, x_dtype, n_tokens, ldx, ws, plan, (hipStream_t)stream));
+}
+
+size_t gptq_prepare_workspace(int64_t d) {
+  if (d <= 0) return 0;
+  return gptq::prepare_workspace(d);
+}
+
+int gptq_prepare_hinv(float* H, int64_t d, double damp, float* U, uint8_t* dead,
+                      int32_t* dev_status, void* ws, size_t ws_bytes, gptq_stream stream) {
+  if (d <= 0 || d > 65536 || !H || !U || !dev_status) return GPTQ_EINVAL;
+  if (!(damp >= 0.0) || !(damp < 1e30)) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::prepare_workspace(d) || !ws || !aligned256(ws)) return GPTQ_EINVAL;
+  return hip_status(
+      gptq::prepare_launch(H, d, damp, U, dead, dev_status, ws, (hipStream_t)stream));
+}
+
+size_t gptq_quantize_workspace(int64_t d_out, int64_t d_in, int block) {
+  if (d_out < 0 || d_in <= 0) return 0;
+  return gptq::quantize_workspace(d_out, d_in, block);
+}
+
+int gptq_quantize_layer(const void* W, int w_dtype, int64_t d_out, int64_t d_in, const float* U,
+                        const uint8_t* dead, int bits, int group_size, int sym, int block,
+                        uint8_t* codes, float* scales, float* zeros, float* loss_rows, void* ws,
+                        size_t ws_bytes, gptq_stream stream) {
+  if (d_out < 0 || d_in <= 0 || d_in > 65536) return GPTQ_EINVAL;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (bits != 2 && bits != 3 && bits != 4) return (bits == 8) ? GPTQ_EUNSUPPORTED : GPTQ_EINVAL;
+  if (!valid_group(d_in, group_size)) return GPTQ_EINVAL;
+  if (!supported_group(group_size)) return GPTQ_EUNSUPPORTED;
+  if (sym != 0 && sym != 1) return GPTQ_EINVAL;
+  if (block != 128) return GPTQ_EUNSUPPORTED;
+  if (d_out == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::quantize_workspace(d_out, d_in, block) || !ws || !aligned256(ws))
+    return GPTQ_EINVAL;
+  return hip_status(gptq::quantize_launch(W, w_dtype, d_out, d_in, U, dead, bits, group_size, sym,
+                                          codes, scales, zeros, loss_rows, ws,
+                                          (hipStream_t)stream));
+}
+
+int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int64_t d_out,
+              int64_t d_in, int bits, int group_size, int sym, uint32_t* qweight,
+              uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream) {
+  if (d_out < 0 || d_in <= 0) return GPTQ_EINVAL;
+  if (bits != 2 && bits != 3 && bits != 4) return GPTQ_EINVAL;
+  if (!valid_group(d_in, group_size)) return GPTQ_EINVAL;
+  if (sym != 0 && sym != 1) return GPTQ_EINVAL;
+  if (d_out == 0) return GPTQ_OK;
+  if (!codes || !scales || !qweight || !scales_f16) return GPTQ_EINVAL;
+  if (!sym && (!zeros || !zeros_f16)) return GPTQ_EINVAL;
+  const int n_groups = (group_size == -1) ? 1 : (int)(d_in / group_size);
+  return hip_status(gptq::pack_launch(codes, scales, zeros, d_out, d_in, bits, n_groups, sym,
+                                      qweight, scales_f16, zeros_f16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,43 @@
+// Internal launchers behind the C ABI (include/gptq.h).  Each returns the
+// hipError_t of its launches; argument validation happens in gptq_abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace gptq {
+
+// ---- Hessian: H(lower) += 2 X^T X --------------------------------------
+struct SyrkPlan {
+  int tile;        // output tile edge (256 for bf16, 64 for fp32)
+  int ntile;       // tiles per dimension
+  int ntri;        // lower-triangle tiles
+  int splits;      // token splits (multiple of 8)
+  int64_t kper;    // tokens per split
+  size_t partial_bytes; // split-K partial tiles
+  size_t ws_bytes;      // partials + per-tile arrival counters
+};
+SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype);
+hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n, int64_t ldx,
+                       void* ws, const SyrkPlan& plan, hipStream_t stream);
+
+// ---- prepare: dead channels, damping, factorization, U ------------------
+size_t prepare_workspace(int64_t d);
+hipError_t prepare_launch(float* H, int64_t d, double damp, float* U, uint8_t* dead,
+                          int32_t* dev_status, void* ws, hipStream_t stream);
+
+// ---- quantize ------------------------------------------------------------
+size_t quantize_workspace(int64_t d_out, int64_t d_in, int block);
+hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                           const float* U, const uint8_t* dead, int bits, int group_size,
+                           int sym, uint8_t* codes, float* scales, float* zeros,
+                           float* loss_rows, void* ws, hipStream_t stream);
+
+// ---- pack ----------------------------------------------------------------
+hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* zeros,
+                       int64_t d_out, int64_t d_in, int bits, int n_groups, int sym,
+                       uint32_t* qweight, uint16_t* scales_f16, uint16_t* zeros_f16,
+                       hipStream_t stream);
+
+}  // namespace gptq

@@ -1,0 +1,207 @@
+"""Thin ctypes binding of libgptq_mi355x.so (C ABI in include/gptq.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch provides device memory (tensors, workspaces) and the stream.  The
+functions keep the C names; tensors replace raw pointers, and outputs that the
+caller does not pass in are allocated here with torch.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgptq_mi355x.so")
+
+GPTQ_OK, GPTQ_EINVAL, GPTQ_EUNSUPPORTED, GPTQ_EHIP, GPTQ_ENOTSPD = range(5)
+GPTQ_BF16, GPTQ_F32 = 0, 1
+
+_lib = None
+
+
+class GPTQError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+        self.status = status
+
+
+class NotSPDError(GPTQError):
+    def __init__(self, pivot: int):
+        RuntimeError.__init__(self, f"gptq_prepare_hinv: Hessian not positive definite "
+                                    f"(pivot index {pivot - 1})")
+        self.status = GPTQ_ENOTSPD
+        self.pivot = pivot
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                           "or python -m post_weight_quantization_syrk_amd.build")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I, SZ, D = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    sig = {
+        "gptq_hessian_accumulate": (I, [P, I64, P, I, I64, I64, P, SZ, P]),
+        "gptq_hessian_workspace": (SZ, [I64, I64, I]),
+        "gptq_prepare_hinv": (I, [P, I64, D, P, P, P, P, SZ, P]),
+        "gptq_prepare_workspace": (SZ, [I64]),
+        "gptq_quantize_layer": (I, [P, I, I64, I64, P, P, I, I, I, I, P, P, P, P, P, SZ, P]),
+        "gptq_quantize_workspace": (SZ, [I64, I64, I]),
+        "gptq_pack": (I, [P, P, P, I64, I64, I, I, I, P, P, P, P]),
+        "gptq_strerror": (ctypes.c_char_p, [I]),
+        "gptq_abi_version": (I, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return lib().gptq_strerror(status).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check(status: int, where: str):
+    if status != GPTQ_OK:
+        raise GPTQError(status, where)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor | None:
+    if nbytes == 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GPTQ_BF16
+    if t.dtype == torch.float32:
+        return GPTQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+# --------------------------------------------------------------------------
+def gptq_hessian_workspace(d: int, n_tokens: int, x_dtype: int) -> int:
+    return int(lib().gptq_hessian_workspace(d, n_tokens, x_dtype))
+
+
+def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: torch.Tensor | None = None,
+                            stream=None) -> torch.Tensor:
+    """H (lower triangle) += 2 X^T X.  H [d, d] fp32; X [n, d] (row stride may exceed d)."""
+    d = H.shape[0]
+    if X.dim() != 2 or X.stride(1) != 1 or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be contiguous fp32 [d, d]; X a row-major [n, >=d] matrix")
+    if X.shape[1] < d:
+        raise ValueError("X has fewer columns than d")
+    xd = _dtype_code(X)
+    n = X.shape[0]
+    need = gptq_hessian_workspace(d, n, xd)
+    if ws is None:
+        ws = _workspace(need, H.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), xd, n, X.stride(0), _ptr(ws),
+                                         nbytes, _stream(stream)), "gptq_hessian_accumulate")
+    return H
+
+
+def gptq_prepare_workspace(d: int) -> int:
+    return int(lib().gptq_prepare_workspace(d))
+
+
+def gptq_prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: torch.Tensor | None = None,
+                      dead: torch.Tensor | None = None, status: torch.Tensor | None = None,
+                      ws: torch.Tensor | None = None, stream=None, check: bool = True):
+    """Damp H in place and compute U (U^T U = H^-1).  Returns (U, dead, status).
+
+    With check=True the stream is synchronised and a breakdown raises NotSPDError.
+    """
+    d = H.shape[0]
+    dev = H.device
+    if U is None:
+        U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    if dead is None:
+        dead = torch.empty(d, dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(gptq_prepare_workspace(d), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_prepare_hinv(_ptr(H), d, float(damp), _ptr(U), _ptr(dead), _ptr(status),
+                                   _ptr(ws), nbytes, _stream(stream)), "gptq_prepare_hinv")
+    if check:
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+        st = int(status.item())
+        if st != 0:
+            raise NotSPDError(st)
+    return U, dead, status
+
+
+def gptq_quantize_workspace(d_out: int, d_in: int, block: int = 128) -> int:
+    return int(lib().gptq_quantize_workspace(d_out, d_in, block))
+
+
+def n_groups_for(d_in: int, group_size: int) -> int:
+    return 1 if group_size == -1 else d_in // group_size
+
+
+def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, dead: torch.Tensor | None = None, *,
+                        bits: int = 4, group_size: int = 128, sym: bool = False,
+                        block: int = 128, codes=None, scales=None, zeros=None, loss_rows=None,
+                        want_loss: bool = True, ws=None, stream=None):
+    """Returns (codes uint8, scales fp32, zeros fp32, loss_rows fp32 or None)."""
+    d_out, d_in = W.shape
+    dev = W.device
+    if not W.is_contiguous() or not U.is_contiguous():
+        raise ValueError("W and U must be contiguous")
+    ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
+    if codes is None:
+        codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+    if zeros is None:
+        zeros = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+    if loss_rows is None and want_loss:
+        loss_rows = torch.empty(d_out, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(gptq_quantize_workspace(d_out, d_in, block), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead),
+                                     bits, group_size, int(bool(sym)), block, _ptr(codes),
+                                     _ptr(scales), _ptr(zeros), _ptr(loss_rows), _ptr(ws),
+                                     nbytes, _stream(stream)), "gptq_quantize_layer")
+    return codes, scales, zeros, loss_rows
+
+
+def gptq_pack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None, *,
+              bits: int, group_size: int, sym: bool, qweight=None, scales_f16=None,
+              zeros_f16=None, stream=None):
+    """Returns (qweight uint32 as int32 tensor, scales_f16 bits, zeros_f16 bits or None)."""
+    d_out, d_in = codes.shape
+    dev = codes.device
+    words = (d_in * bits + 31) // 32
+    ng = n_groups_for(d_in, group_size)
+    if qweight is None:
+        qweight = torch.empty((d_out, words), dtype=torch.int32, device=dev)
+    if scales_f16 is None:
+        scales_f16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    if zeros_f16 is None and not sym:
+        zeros_f16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+    _check(lib().gptq_pack(_ptr(codes), _ptr(scales), _ptr(zeros), d_out, d_in, bits, group_size,
+                           int(bool(sym)), _ptr(qweight), _ptr(scales_f16), _ptr(zeros_f16),
+                           _stream(stream)), "gptq_pack")
+    return qweight, scales_f16, zeros_f16

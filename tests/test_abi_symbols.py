@@ -1,0 +1,84 @@
+"""The C-ABI library loads and exports every entry point include/gptq.h declares.
+
+CPU only: no compute call is made; only host-side queries and the argument
+checks that return before anything is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gptq.h")
+LIB = os.path.join(ROOT, "post_weight_quantization_syrk_amd", "libgptq_mi355x.so")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gptq_[a-z0-9_]+)\s*\(", text)))
+
+
+def _lib():
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    return ctypes.CDLL(LIB)
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("gptq_hessian_accumulate", "gptq_prepare_hinv", "gptq_quantize_layer", "gptq_pack"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_host_queries():
+    from post_weight_quantization_syrk_amd import gptq
+    if not os.path.exists(gptq.LIB_PATH):
+        pytest.skip("library not built")
+    assert gptq.lib().gptq_abi_version() == 100
+    assert gptq.strerror(0) == "ok"
+    assert "positive definite" in gptq.strerror(4)
+    # workspace sizes: split-K partials, factorization scratch, working copies
+    assert gptq.gptq_hessian_workspace(4096, 262144, gptq.GPTQ_BF16) > 0
+    assert gptq.gptq_hessian_workspace(4096, 0, gptq.GPTQ_BF16) == 0
+    assert gptq.gptq_prepare_workspace(4096) >= 2 * 4096 * 4096 * 8
+    assert gptq.gptq_quantize_workspace(4096, 4096) >= 2 * 4096 * 4096 * 4
+
+
+def test_argument_errors_return_before_any_launch():
+    from post_weight_quantization_syrk_amd import gptq
+    if not os.path.exists(gptq.LIB_PATH):
+        pytest.skip("library not built")
+    L = gptq.lib()
+    P = ctypes.c_void_p
+    fake = P(0x1000)  # never dereferenced: every call below fails validation first
+    # bad dtype / sizes
+    assert L.gptq_hessian_accumulate(fake, 16, fake, 7, 10, 16, None, 0, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_hessian_accumulate(fake, 16, fake, 0, 10, 8, None, 0, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_hessian_accumulate(fake, 16, fake, 0, 10, 16, None, 0, None) == gptq.GPTQ_EINVAL  # no ws
+    assert L.gptq_hessian_accumulate(None, 16, fake, 0, 10, 16, None, 0, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_hessian_accumulate(fake, 16, fake, 0, 0, 16, None, 0, None) == gptq.GPTQ_OK  # no-op
+    # prepare: missing workspace, negative damping
+    assert L.gptq_prepare_hinv(fake, 8, 0.01, fake, None, fake, None, 0, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_prepare_hinv(fake, 8, -1.0, fake, None, fake, fake, 1 << 20, None) == gptq.GPTQ_EINVAL
+    # quantize: bits, group size, block
+    q = L.gptq_quantize_layer
+    args = lambda bits, g, sym, block, d_in=256: (fake, 0, 4, d_in, fake, None, bits, g, sym, block,
+                                                   fake, fake, fake, None, None, 0, None)
+    assert q(*args(5, 128, 0, 128)) == gptq.GPTQ_EINVAL
+    assert q(*args(8, 128, 0, 128)) == gptq.GPTQ_EUNSUPPORTED
+    assert q(*args(4, 48, 0, 128)) == gptq.GPTQ_EINVAL       # 48 does not divide 256
+    assert q(*args(4, 16, 0, 128)) == gptq.GPTQ_EUNSUPPORTED  # divides, not implemented
+    assert q(*args(4, 128, 0, 64)) == gptq.GPTQ_EUNSUPPORTED
+    assert q(*args(4, 128, 2, 128)) == gptq.GPTQ_EINVAL
+    assert q(*args(4, 128, 0, 128)) == gptq.GPTQ_EINVAL      # no workspace
+    # pack
+    assert L.gptq_pack(fake, fake, fake, 4, 256, 5, 128, 0, fake, fake, fake, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_pack(fake, fake, None, 4, 256, 4, 128, 0, fake, fake, None, None) == gptq.GPTQ_EINVAL

@@ -1,0 +1,313 @@
+"""GPU parity: every stage of the HIP path, called through the C ABI, against
+the float64 oracle on the same seeded inputs.  Needs an MI355X."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from post_weight_quantization_syrk_amd import gptq, synth
+from parity import compare_quant, h_rel_error
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    gptq.lib()  # loud failure if the library is missing
+
+
+def dev_bf16(bits_u16: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(DEV).view(torch.bfloat16)
+
+
+def dev_f32(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(DEV)
+
+
+def to_dev(a, dtype):
+    return dev_bf16(a) if dtype == "bf16" else dev_f32(a)
+
+
+def rand_x(n, d, dtype, seed, ld=None):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n, ld or d), dtype=np.float32) * np.exp(
+        rng.standard_normal(ld or d)).astype(np.float32)
+    if dtype == "bf16":
+        b = synth.f32_to_bf16_bits(x)
+        return b, synth.as_f64(b, "bf16")[:, :d]
+    return x, x.astype(np.float64)[:, :d]
+
+
+# ------------------------------------------------------------------ Hessian
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n,d", [(1, 1), (100, 37), (1000, 300), (3000, 513), (640, 256)])
+def test_hessian_small_ragged(dtype, n, d):
+    print(f"[hessian] dtype={dtype} n={n} d={d}", flush=True)
+    xs, x64 = rand_x(n, d, dtype, seed=n * 7 + d)
+    X = to_dev(xs, dtype)
+    H = torch.zeros((d, d), dtype=torch.float32, device=DEV)
+    sentinel = 12345.0
+    H += torch.triu(torch.full((d, d), sentinel, device=DEV), 1)
+    gptq.gptq_hessian_accumulate(H, X)
+    Hn = H.cpu().numpy()
+    ref = oracle.hessian([x64])
+    assert h_rel_error(Hn, ref) <= 1e-5 if dtype == "f32" else h_rel_error(Hn, ref) <= 1e-5
+    assert np.all(np.triu(Hn, 1) == np.triu(np.full((d, d), sentinel, np.float32), 1))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hessian_strided_rows_and_accumulation(dtype):
+    n, d, ld = 2000, 200, 203     # odd row stride: unaligned rows, scalar load path
+    xs, x64 = rand_x(n, d, dtype, seed=5, ld=ld)
+    X = to_dev(xs, dtype)
+    H = torch.zeros((d, d), dtype=torch.float32, device=DEV)
+    gptq.gptq_hessian_accumulate(H, X[:700])
+    gptq.gptq_hessian_accumulate(H, X[700:])
+    assert h_rel_error(H.cpu().numpy(), oracle.hessian([x64])) <= 1e-5
+
+
+def test_hessian_deterministic():
+    xs, _ = rand_x(5000, 640, "bf16", seed=9)
+    X = dev_bf16(xs)
+    outs = []
+    for _ in range(2):
+        H = torch.zeros((640, 640), dtype=torch.float32, device=DEV)
+        gptq.gptq_hessian_accumulate(H, X)
+        outs.append(H.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
+
+
+def test_hessian_small_workload():
+    wl = synth.SMALL
+    xs = synth.x_chunk(wl, 0)
+    H = torch.zeros((wl.d_in, wl.d_in), dtype=torch.float32, device=DEV)
+    gptq.gptq_hessian_accumulate(H, dev_f32(xs))
+    ref = oracle.hessian([synth.as_f64(xs, "f32")])
+    assert h_rel_error(H.cpu().numpy(), ref) <= 1e-6
+
+
+def test_hessian_full_size_sampled():
+    """Full 4096-wide layer over 262144 bf16 tokens (the benchmark's launch
+    configuration); entries sampled and recomputed one by one by the oracle."""
+    wl = synth.ATTN7B
+    print("[hessian full] generating X", flush=True)
+    xb = synth.x_full(wl)
+    X = dev_bf16(xb)
+    H = torch.zeros((wl.d_in, wl.d_in), dtype=torch.float32, device=DEV)
+    gptq.gptq_hessian_accumulate(H, X)
+    Hn = H.cpu().numpy()
+    del X
+    rng = np.random.default_rng(0)
+    idx = rng.integers(0, wl.d_in, size=(48, 2))
+    idx = np.concatenate([idx, np.stack([np.arange(0, 4096, 512)] * 2, 1)])
+    x32 = synth.bf16_bits_to_f32(xb[:, np.unique(idx)])
+    col = {c: k for k, c in enumerate(np.unique(idx))}
+    diag = {}
+    for c in np.unique(idx):
+        diag[c] = oracle.hessian_entry(x32, col[c], col[c])
+    errs = []
+    for i, j in idx:
+        i, j = max(i, j), min(i, j)
+        ref = oracle.hessian_entry(x32, col[i], col[j])
+        errs.append(abs(float(Hn[i, j]) - ref) / np.sqrt(diag[i] * diag[j]))
+    print(f"[hessian full] max normalized entry error {max(errs):.3e}", flush=True)
+    assert max(errs) <= 1e-4
+
+
+# ------------------------------------------------------------ factorization
+def _spd(d, seed, n=None):
+    rng = np.random.default_rng(seed)
+    n = n or 3 * d
+    x = rng.standard_normal((n, d)) @ (np.eye(d) + 0.3 * rng.standard_normal((d, d)) / np.sqrt(d))
+    x *= np.exp(0.5 * rng.standard_normal(d))
+    return (2.0 * x.T @ x).astype(np.float32)
+
+
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 256, 1000])
+def test_prepare_matches_oracle(d):
+    H32 = _spd(d, d)
+    H = dev_f32(np.tril(H32))
+    U, dead, status = gptq.gptq_prepare_hinv(H, damp=0.01)
+    ref = oracle.prepare(H32.astype(np.float64), 0.01)
+    Ug = U.cpu().numpy().astype(np.float64)
+    err = np.max(np.abs(Ug - ref["U"])) / np.max(np.abs(ref["U"]))
+    print(f"[prepare] d={d} max rel U err {err:.2e}", flush=True)
+    assert err <= 2e-6
+    assert np.all(np.tril(Ug, -1) == 0)
+    np.testing.assert_allclose(H.cpu().numpy(), ref["H"], rtol=2e-7, atol=0)
+    assert not dead.cpu().numpy().any()
+
+
+def test_prepare_dead_channels_and_identity():
+    d = 130
+    H32 = _spd(d, 3)
+    H32[:, [4, 77]] = 0
+    H32[[4, 77], :] = 0
+    H = dev_f32(H32)
+    U, dead, _ = gptq.gptq_prepare_hinv(H)
+    ref = oracle.prepare(H32.astype(np.float64))
+    assert dead.cpu().numpy().astype(bool).tolist() == ref["dead"].tolist()
+    err = np.max(np.abs(U.cpu().numpy() - ref["U"])) / np.max(np.abs(ref["U"]))
+    assert err <= 2e-6
+    # H = 2I: U is exactly diagonal
+    U, _, _ = gptq.gptq_prepare_hinv(dev_f32(2 * np.eye(256)))
+    Un = U.cpu().numpy()
+    assert np.count_nonzero(Un - np.diag(np.diag(Un))) == 0
+
+
+def test_prepare_not_spd():
+    d = 70
+    with pytest.raises(gptq.NotSPDError) as e:
+        gptq.gptq_prepare_hinv(dev_f32(-np.eye(d)))
+    assert e.value.pivot == d  # elimination starts at index d-1
+    with pytest.raises(oracle.NotSPD):
+        oracle.prepare(-np.eye(d))
+    # indefinite with a positive diagonal
+    A = np.eye(4, dtype=np.float32)
+    A[3, 2] = A[2, 3] = 2.0
+    with pytest.raises(gptq.NotSPDError):
+        gptq.gptq_prepare_hinv(dev_f32(A), damp=0.0)
+    with pytest.raises(oracle.NotSPD):
+        oracle.prepare(A.astype(np.float64), damp=0.0)
+
+
+# ---------------------------------------------------------------- quantizer
+QCASES = [(4, 128, False), (4, 64, True), (3, 64, True), (3, 32, False), (2, 32, False),
+          (4, -1, False), (2, -1, True)]
+
+
+def _gpu_quant(W_dev, U, dead, bits, g, sym):
+    codes, scales, zeros, loss = gptq.gptq_quantize_layer(W_dev, U, dead, bits=bits, group_size=g,
+                                                          sym=sym)
+    torch.cuda.synchronize()
+    return dict(codes=codes.cpu().numpy(), scales=scales.cpu().numpy(),
+                zeros=zeros.cpu().numpy(), loss=loss.cpu().numpy())
+
+
+@pytest.mark.parametrize("bits,g,sym", QCASES)
+@pytest.mark.parametrize("d_out,d_in", [(37, 256), (16, 128), (5, 320), (64, 384)])
+def test_identity_hessian_bit_exact_rtn(bits, g, sym, d_out, d_in):
+    if g > 0 and d_in % g:
+        pytest.skip("group must divide d_in")
+    print(f"[rtn] bits={bits} g={g} sym={sym} {d_out}x{d_in}", flush=True)
+    rng = np.random.default_rng(bits * 1000 + d_in + d_out)
+    W = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    W[d_out // 2, d_in // 3] = 0.7
+    W[0, :32] = 0.0  # a degenerate group
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(2 * np.eye(d_in)))
+    out = _gpu_quant(dev_f32(W), U, dead, bits, g, sym)
+    ref = oracle.rtn(W.astype(np.float64), bits=bits, group_size=g, sym=sym)
+    np.testing.assert_array_equal(out["scales"], ref["scales"])
+    np.testing.assert_array_equal(out["zeros"], ref["zeros"])
+    np.testing.assert_array_equal(out["codes"], ref["codes"])
+
+
+@pytest.mark.parametrize("bits,g,sym", QCASES)
+def test_quantize_parity_correlated(bits, g, sym):
+    d_out, d_in = 96, 384
+    H32 = _spd(d_in, 11)
+    rng = np.random.default_rng(12)
+    W = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(H32))
+    out = _gpu_quant(dev_f32(W), U, dead, bits, g, sym)
+    p = oracle.prepare(H32.astype(np.float64))
+    ref = oracle.gptq(W, p["U"], p["dead"], bits=bits, group_size=g, sym=sym, block=128)
+    rep = compare_quant(out, ref, group_size=g, bits=bits, W=W.astype(np.float64),
+                        H0=H32.astype(np.float64))
+    print(f"[quant] bits={bits} g={g} sym={sym} {rep}", flush=True)
+    # the damped-H loss identity holds on the GPU side too
+    np.testing.assert_allclose(out["loss"], ref["loss_damped"], rtol=5e-3)
+
+
+def test_quantize_empty_rows():
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(2 * np.eye(128)))
+    W = torch.zeros((0, 128), dtype=torch.float32, device=DEV)
+    codes, scales, zeros, _ = gptq.gptq_quantize_layer(W, U, dead)
+    assert codes.shape == (0, 128)
+
+
+# --------------------------------------------------------------------- pack
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d_in,g,sym", [(32, 32, False), (100, -1, True), (4096, 128, False),
+                                        (320, 64, True)])
+def test_pack_bit_exact(bits, d_in, g, sym):
+    rng = np.random.default_rng(bits + d_in)
+    d_out = 7
+    codes = rng.integers(0, 1 << bits, size=(d_out, d_in), dtype=np.uint8)
+    ng = 1 if g == -1 else d_in // g
+    scales = oracle.fp16_rne(np.exp(rng.standard_normal((d_out, ng)) - 5))
+    zeros = rng.integers(0, 1 << bits, size=(d_out, ng)).astype(np.float64)
+    cd = torch.from_numpy(codes).to(DEV)
+    qw, s16, z16 = gptq.gptq_pack(cd, dev_f32(scales), dev_f32(zeros), bits=bits, group_size=g,
+                                  sym=sym)
+    torch.cuda.synchronize()
+    ref = oracle.pack_rows(codes, bits)
+    np.testing.assert_array_equal(qw.cpu().numpy().view(np.uint32), ref)
+    np.testing.assert_array_equal(s16.cpu().numpy().view(np.uint16), oracle.fp16_bits(scales))
+    if not sym:
+        np.testing.assert_array_equal(z16.cpu().numpy().view(np.uint16), oracle.fp16_bits(zeros))
+
+
+# -------------------------------------------------------------- end to end
+def _e2e(wl: synth.Workload, tensor=0):
+    """All four calls through the C ABI vs the oracle on the same inputs."""
+    print(f"[e2e] {wl.name}", flush=True)
+    Wst = synth.w_matrix(wl, tensor)
+    W64 = synth.as_f64(Wst, wl.w_dtype)
+    chunks = [synth.x_chunk(wl, c) for c in range(synth.n_chunks(wl))]
+    H = torch.zeros((wl.d_in, wl.d_in), dtype=torch.float32, device=DEV)
+    for xc in chunks:
+        gptq.gptq_hessian_accumulate(H, to_dev(xc, wl.x_dtype))
+    H_gpu = H.cpu().numpy()
+    U, dead, _ = gptq.gptq_prepare_hinv(H, damp=wl.damp)
+    out = _gpu_quant(to_dev(Wst, wl.w_dtype), U, dead, wl.bits, wl.group_size, wl.sym)
+    H0 = oracle.hessian(synth.as_f64(xc, wl.x_dtype) for xc in chunks)
+    assert h_rel_error(H_gpu, H0) <= 1e-4
+    p = oracle.prepare(H0, wl.damp)
+    ref = oracle.gptq(W64, p["U"], p["dead"], bits=wl.bits, group_size=wl.group_size,
+                      sym=wl.sym, block=wl.block)
+    rep = compare_quant(out, ref, group_size=wl.group_size, bits=wl.bits, W=W64, H0=H0)
+    print(f"[e2e] {wl.name}: {rep}", flush=True)
+    return rep
+
+
+def test_e2e_small_workload():
+    _e2e(synth.SMALL)
+
+
+@pytest.mark.parametrize("wl", [
+    synth.scaled(synth.ATTN7B, d_out=512, d_in=1024, n_tokens=16384, chunk_tokens=4096),
+    synth.scaled(synth.FFN_GATE, d_out=700, d_in=512, n_tokens=8192, chunk_tokens=4096),
+    synth.scaled(synth.FFN_DOWN, d_out=256, d_in=1408, n_tokens=8192, chunk_tokens=4096),
+    synth.scaled(synth.L70B_SQ, d_out=300, d_in=1024, n_tokens=8192, bits=2, group_size=32),
+    synth.scaled(synth.L70B_SQ, d_out=300, d_in=1024, n_tokens=8192, bits=4, group_size=-1),
+], ids=lambda w: w.name)
+def test_e2e_scaled_workloads(wl):
+    _e2e(wl)
+
+
+def test_quantize_full_size_attention_layer():
+    """4096 x 4096 bf16 layer at full size, stage-isolated from the Hessian:
+    the oracle's own H from 16384 seeded tokens feeds both sides."""
+    wl = synth.ATTN7B
+    sub = synth.scaled(wl, n_tokens=16384, chunk_tokens=8192)
+    H0 = oracle.hessian(synth.as_f64(synth.x_chunk(sub, c), "bf16") for c in range(2))
+    H32 = np.tril(H0).astype(np.float32)
+    H0r = np.tril(H32).astype(np.float64)
+    H0r = H0r + np.tril(H0r, -1).T
+    Wst = synth.w_matrix(wl)
+    W64 = synth.as_f64(Wst, "bf16")
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(H32), damp=wl.damp)
+    out = _gpu_quant(dev_bf16(Wst), U, dead, wl.bits, wl.group_size, wl.sym)
+    print("[quant full] oracle running", flush=True)
+    p = oracle.prepare(H0r, wl.damp)
+    ref = oracle.gptq(W64, p["U"], p["dead"], bits=wl.bits, group_size=wl.group_size,
+                      sym=wl.sym, block=128)
+    rep = compare_quant(out, ref, group_size=wl.group_size, bits=wl.bits, W=W64, H0=H0r)
+    print(f"[quant full] {rep}", flush=True)
