@@ -187,7 +187,7 @@ def main():
     trail_flops = float(d_out) * d_in * (d_in - wl.block)
     syrk_tflops = syrk_flops / (stage_ms["hessian"] / 1e3) / 1e12
     roofline = {
-        "kernel": "syrk_bf16_kernel (H += 2 X^T X, incl. fused split-K reduction)",
+        "kernel": "syrk_bf16_async_kernel (H += 2 X^T X, incl. fused split-K reduction)",
         "bound": "mfma",
         "achieved": round(syrk_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,

@@ -83,7 +83,8 @@ size_t gptq_hessian_workspace(int64_t d, int64_t n_tokens, int x_dtype);
  * Then U [d x d] float32 is written: the upper triangular matrix with positive
  * diagonal and U^T U = H^{-1} (the strict lower triangle of U is set to 0).
  * It is computed as U = V^{-1} where H = V V^T with V upper triangular, which
- * is the same unique factor as chol(H^{-1}); arithmetic is float64.
+ * is the same unique factor as chol(H^{-1}); arithmetic is fp32 (the lambda
+ * shift is formed in float64).
  *
  * dead       [d] uint8 out, may be NULL.
  * dev_status [1] int32 out (device): 0 on success, otherwise 1 + the index

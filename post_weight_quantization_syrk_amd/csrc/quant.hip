@@ -14,6 +14,7 @@
 //              GEMM (v_mfma_f32_32x32x2f32), K = 128.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_f32.h"
 
 #include <hip/hip_fp16.h>
 #include <algorithm>
@@ -39,6 +40,15 @@ QuantWs carve(void* ws, int64_t d_out, int64_t d_in) {
   w.Err = (float*)((char*)ws + m);
   return w;
 }
+
+// Quantizer shape, uniform over the launch.
+struct QSpec {
+  int maxq;     // 2^bits - 1
+  int sym;      // 0 asymmetric, 1 symmetric
+  int gsize;    // group size (power of two, <= 128), 0 = one group per row
+  int gshift;   // log2(gsize)
+  int n_groups;
+};
 
 // One rounding of a positive float64 to binary16, nearest-even.  Returns the
 // binary16 value as a float64 (0 when it underflows, +inf on overflow).
@@ -72,13 +82,13 @@ struct GroupParams {
   float s, inv_s, hs, z;
 };
 
-template <int BITS, bool SYM>
-__device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi) {
-  constexpr int maxq = (1 << BITS) - 1;
+// Scale and zero from the group's min/max (asymmetric) or max |v| (symmetric).
+// The step is formed in float64 and rounded once to binary16.
+__device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi, int maxq, int sym) {
   GroupParams p;
   double s;
   float z;
-  if (SYM) {
+  if (sym) {
     const double amax = (double)lo_or_amax;
     s = f64_to_f16_value(2.0 * amax / (double)maxq);
     z = (float)((maxq + 1) / 2);
@@ -103,9 +113,10 @@ __device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi) {
 }
 
 // Nearest integer to the exact quotient x/s, ties to even, then code clamp.
-template <int BITS>
-__device__ __forceinline__ float quantize_code(float x, const GroupParams& p) {
-  constexpr float maxq = (float)((1 << BITS) - 1);
+// q0 = rint(x * (1/s)) is within 1 of it; the exact comparisons against
+// (q0 +- 1/2) s (products of <= 12-bit and 11-bit integers: exact in fp32)
+// settle the last unit.
+__device__ __forceinline__ float quantize_code(float x, const GroupParams& p, float maxq) {
   float q0 = rintf(x * p.inv_s);
   q0 = fminf(fmaxf(q0, -2047.0f), 2047.0f);
   const float up = fmaf(q0, p.s, p.hs);    // (q0 + 1/2) s, exact
@@ -118,10 +129,9 @@ __device__ __forceinline__ float quantize_code(float x, const GroupParams& p) {
   return fminf(fmaxf(q0 + p.z, 0.0f), maxq);
 }
 
-// g = -1: one group per row from the whole (current = original) row.
-template <int BITS, bool SYM>
+// One group per row: parameters from the whole (current = original) row.
 __global__ __launch_bounds__(256) void rowparams_kernel(const float* __restrict__ Wc,
-                                                        int64_t d_out, int64_t d_in,
+                                                        int64_t d_out, int64_t d_in, QSpec q,
                                                         float* __restrict__ scales,
                                                         float* __restrict__ zeros) {
   const int lane = threadIdx.x & 63;
@@ -131,25 +141,21 @@ __global__ __launch_bounds__(256) void rowparams_kernel(const float* __restrict_
   float mn = 0.0f, mx = 0.0f;  // the range always contains 0
   for (int64_t c = lane; c < d_in; c += 64) {
     const float v = w[c];
-    if (SYM) {
-      mx = fmaxf(mx, fabsf(v));
-    } else {
-      mn = fminf(mn, v);
-      mx = fmaxf(mx, v);
-    }
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, q.sym ? fabsf(v) : v);
   }
   for (int m = 32; m > 0; m >>= 1) {
     mn = fminf(mn, __shfl_xor(mn, m, 64));
     mx = fmaxf(mx, __shfl_xor(mx, m, 64));
   }
   if (lane == 0) {
-    const GroupParams p = SYM ? make_params<BITS, true>(mx, 0.0f) : make_params<BITS, false>(mn, mx);
+    const GroupParams p = q.sym ? make_params(mx, 0.0f, q.maxq, 1) : make_params(mn, mx, q.maxq, 0);
     scales[row] = p.s;
     zeros[row] = p.z;
   }
 }
 
-// Broadcast lane `src` (0..15) of each 16-lane row to the whole row.
+// Broadcast lane `SRC` (0..15) of each 16-lane row to the whole row.
 template <int SRC>
 __device__ __forceinline__ float row_bcast(float v) {
   return __int_as_float(
@@ -167,104 +173,86 @@ __device__ __forceinline__ float row_max(float v) {
   return v;
 }
 
-template <int J>
-struct BcastAt {
-  static __device__ __forceinline__ float get(const float (&w)[8]) {
-    return row_bcast<J / 8>(w[J % 8]);
-  }
-};
-
-// G = 0 means one group per row with parameters precomputed by rowparams_kernel.
-template <int BITS, int G, bool SYM>
 __global__ __launch_bounds__(256) void colloop_kernel(
     float* __restrict__ Wc, float* __restrict__ Err, const float* __restrict__ U,
-    int64_t d_out, int64_t d_in, int64_t b0, uint8_t* __restrict__ codes,
-    float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows,
-    int n_groups) {
+    int64_t d_out, int64_t d_in, int64_t b0, QSpec q, uint8_t* __restrict__ codes,
+    float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows) {
   __shared__ __attribute__((aligned(16))) float us[QB * UPITCH];
   __shared__ float invd[QB];
   const int tid = threadIdx.x;
   const int bw = (int)min<int64_t>(QB, d_in - b0);
+  const int c = tid & 15;  // lane within the row group
+  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const bool live = row < d_out;
+  const int64_t rr = live ? row : 0;
+  const float maxq = (float)q.maxq;
+  float w[8];
+  {
+    // this lane's 8 columns of the row (unconditional loads, masked after)
+    const float* src = Wc + rr * d_in + b0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = src[min(8 * c + i, bw - 1)];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = (8 * c + i < bw) ? w[i] : 0.0f;
+  }
   // U block: upper triangle only, identity padding past the matrix edge.
-  for (int e = tid; e < QB * QB; e += 256) {
-    const int r = e >> 7, c = e & 127;
-    float v;
-    if (r < bw && c < bw)
-      v = (c >= r) ? U[(b0 + r) * d_in + b0 + c] : 0.0f;
-    else
-      v = (r == c) ? 1.0f : 0.0f;
-    us[r * UPITCH + c] = v;
+  // 64 elements per thread, loaded in batches of 16 with clamped addresses.
+#pragma unroll
+  for (int b = 0; b < QB * QB / 256; b += 16) {
+    float v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = (b + u) * 256 + tid, r = e >> 7, cc = e & 127;
+      v[u] = U[(b0 + min(r, bw - 1)) * d_in + b0 + min(cc, bw - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = (b + u) * 256 + tid, r = e >> 7, cc = e & 127;
+      us[r * UPITCH + cc] = (r < bw && cc < bw) ? (cc >= r ? v[u] : 0.0f) : (r == cc ? 1.0f : 0.0f);
+    }
   }
   __syncthreads();
   if (tid < QB) invd[tid] = 1.0f / us[tid * UPITCH + tid];
   __syncthreads();
 
-  const int c = tid & 15;                  // lane within the row group
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
-  const bool live = row < d_out;
-  const int64_t rr = live ? row : 0;
-  float w[8];
-  {
-    const float* src = Wc + rr * d_in + b0 + 8 * c;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = (8 * c + i < bw && live) ? src[i] : 0.0f;
-  }
   GroupParams gp;
-  if (G == 0) {
-    gp = make_params<BITS, SYM>(0.0f, 0.0f);
+  if (q.gsize == 0) {
     gp.s = scales[rr];
     gp.inv_s = 1.0f / gp.s;
     gp.hs = 0.5f * gp.s;
     gp.z = zeros[rr];
   }
+  const int gmask = q.gsize - 1;
   float cr[8], er[8];
   float loss = 0.0f;
+  // Fully unrolled over the 128 columns: register indices and the DPP source
+  // lane are compile-time constants.
+  StaticFor<0, QB>::run([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    if (j >= bw) return;
+    if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
+      if (q.gsize != 0 && (j & gmask) == 0) {
+        const bool mine = (8 * c >= j) && (8 * c < j + q.gsize);
+        float mn = 0.0f, mx = 0.0f;
+        if (mine) {
 #pragma unroll
-  for (int j = 0; j < QB; ++j) {
-    if (j >= bw) continue;
-    if (G > 0 && (j % (G > 0 ? G : 1)) == 0) {
-      const bool mine = (8 * c >= j) && (8 * c < j + G);
-      float mn = 0.0f, mx = 0.0f;
-      if (mine) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          if (SYM) {
-            mx = fmaxf(mx, fabsf(w[i]));
-          } else {
+          for (int i = 0; i < 8; ++i) {
             mn = fminf(mn, w[i]);
-            mx = fmaxf(mx, w[i]);
+            mx = fmaxf(mx, q.sym ? fabsf(w[i]) : w[i]);
           }
         }
-      }
-      mx = row_max(mx);
-      if (!SYM) mn = row_min(mn);
-      gp = SYM ? make_params<BITS, true>(mx, 0.0f) : make_params<BITS, false>(mn, mx);
-      if (c == (j >> 3) && live) {
-        const int64_t gi = rr * n_groups + (b0 + j) / G;
-        scales[gi] = gp.s;
-        zeros[gi] = gp.z;
+        mx = row_max(mx);
+        mn = row_min(mn);
+        gp = q.sym ? make_params(mx, 0.0f, q.maxq, 1) : make_params(mn, mx, q.maxq, 0);
+        if (c == (j >> 3) && live) {
+          const int64_t gi = rr * q.n_groups + ((b0 + j) >> q.gshift);
+          scales[gi] = gp.s;
+          zeros[gi] = gp.z;
+        }
       }
     }
-    float x;
-    switch (j >> 3) {
-      case 0: x = row_bcast<0>(w[j & 7]); break;
-      case 1: x = row_bcast<1>(w[j & 7]); break;
-      case 2: x = row_bcast<2>(w[j & 7]); break;
-      case 3: x = row_bcast<3>(w[j & 7]); break;
-      case 4: x = row_bcast<4>(w[j & 7]); break;
-      case 5: x = row_bcast<5>(w[j & 7]); break;
-      case 6: x = row_bcast<6>(w[j & 7]); break;
-      case 7: x = row_bcast<7>(w[j & 7]); break;
-      case 8: x = row_bcast<8>(w[j & 7]); break;
-      case 9: x = row_bcast<9>(w[j & 7]); break;
-      case 10: x = row_bcast<10>(w[j & 7]); break;
-      case 11: x = row_bcast<11>(w[j & 7]); break;
-      case 12: x = row_bcast<12>(w[j & 7]); break;
-      case 13: x = row_bcast<13>(w[j & 7]); break;
-      case 14: x = row_bcast<14>(w[j & 7]); break;
-      default: x = row_bcast<15>(w[j & 7]); break;
-    }
-    const float code = quantize_code<BITS>(x, gp);
+    const float x = row_bcast<(j >> 3)>(w[j & 7]);
+    const float code = quantize_code(x, gp, maxq);
     const float what = gp.s * (code - gp.z);
     const float delta = (x - what) * invd[j];
     loss = fmaf(delta, delta, loss);
@@ -272,10 +260,17 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       cr[j & 7] = code;
       er[j & 7] = delta;
     }
-    const float* urow = us + j * UPITCH + 8 * c;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = fmaf(-delta, urow[i], w[i]);
-  }
+    const float4* urow = (const float4*)(us + j * UPITCH + 8 * c);
+    const float4 u0 = urow[0], u1 = urow[1];
+    w[0] = fmaf(-delta, u0.x, w[0]);
+    w[1] = fmaf(-delta, u0.y, w[1]);
+    w[2] = fmaf(-delta, u0.z, w[2]);
+    w[3] = fmaf(-delta, u0.w, w[3]);
+    w[4] = fmaf(-delta, u1.x, w[4]);
+    w[5] = fmaf(-delta, u1.y, w[5]);
+    w[6] = fmaf(-delta, u1.z, w[6]);
+    w[7] = fmaf(-delta, u1.w, w[7]);
+  });
   if (!live) return;
   // codes and scaled errors of this lane's 8 columns
   uint8_t* cdst = codes + rr * d_in + b0 + 8 * c;
@@ -290,106 +285,28 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]   (fp32 MFMA, 128 x 128 tiles)
+// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]   (fp32 MFMA, 128 x 128 tiles, K = 128)
+using TrailTile = MfmaTile<128, 128, QB, false>;
+
 __global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc,
                                                        const float* __restrict__ Err,
                                                        const float* __restrict__ U,
                                                        int64_t d_out, int64_t d_in, int64_t b0,
                                                        int kb, int64_t n0) {
-  constexpr int T = 128;
-  // sa[k][m] = Err[m0+m][b0+k], sb[k][n] = U[b0+k][n0t+n]; odd k rows are stored
-  // with column index ^ 32 so the two 32-lane halves of an MFMA operand read
-  // (rows k and k+1) fall in different LDS banks.
-  __shared__ float sa[QB][T];
-  __shared__ float sb[QB][T];
+  __shared__ __attribute__((aligned(16))) float lds[TrailTile::lds_floats];
   const int64_t ncols = d_in - n0;
-  const int ntn = (int)ceil_div(ncols, T);
-  const int64_t m0 = (int64_t)(blockIdx.x / ntn) * T;
-  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * T;
-  const int tid = threadIdx.x;
-  for (int e = tid; e < T * QB; e += 256) {
-    const int m = e >> 7, k = e & 127;  // consecutive threads: consecutive k
-    const int64_t gm = m0 + m;
-    sa[k][m ^ ((k & 1) << 5)] = (gm < d_out && k < kb) ? Err[gm * d_in + b0 + k] : 0.0f;
-  }
-  for (int e = tid; e < QB * T; e += 256) {
-    const int k = e >> 7, n = e & 127;
-    const int64_t gn = n0t + n;
-    sb[k][n ^ ((k & 1) << 5)] = (k < kb && gn < d_in) ? U[(b0 + k) * d_in + gn] : 0.0f;
-  }
+  const int ntn = (int)ceil_div(ncols, 128);
+  const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
+  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * 128;
+  const int rows = (int)min<int64_t>(128, d_out - m0);
+  const int cols = (int)min<int64_t>(128, d_in - n0t);
+  f32x16 acc[TrailTile::FM][TrailTile::FN];
+  TrailTile::zero(acc);
+  TrailTile::load_p(lds, Err + m0 * d_in + b0, d_in, rows, kb);
+  TrailTile::load_q(lds, U + b0 * d_in + n0t, d_in, kb, cols);
   __syncthreads();
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
-  const int kl = lane >> 5, ml = lane & 31;
-#pragma unroll 4
-  for (int k = 0; k < QB; k += 2) {
-    float av[2], bv[2];
-#pragma unroll
-    for (int a = 0; a < 2; ++a) av[a] = sa[k + kl][(64 * wm + 32 * a + ml) ^ (kl << 5)];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) bv[b] = sb[k + kl][(64 * wn + 32 * b + ml) ^ (kl << 5)];
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[a], bv[b], acc[a][b], 0, 0, 0);
-  }
-#pragma unroll
-  for (int a = 0; a < 2; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t gm = m0 + 64 * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t gn = n0t + 64 * wn + 32 * b + (lane & 31);
-        if (gm < d_out && gn < d_in) {
-          float* p = Wc + gm * d_in + gn;
-          *p = *p - acc[a][b][r];
-        }
-      }
-}
-
-template <int BITS, int G, bool SYM>
-hipError_t run_quant(float* Wc, float* Err, const float* U, int64_t d_out, int64_t d_in,
-                     uint8_t* codes, float* scales, float* zeros, float* loss_rows,
-                     int n_groups, hipStream_t stream) {
-  if (G == 0)
-    hipLaunchKernelGGL((rowparams_kernel<BITS, SYM>), dim3((unsigned)ceil_div(d_out, 4)),
-                       dim3(256), 0, stream, (const float*)Wc, d_out, d_in, scales, zeros);
-  const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
-  for (int64_t b0 = 0; b0 < d_in; b0 += QB) {
-    hipLaunchKernelGGL((colloop_kernel<BITS, G, SYM>), dim3(rgrid), dim3(256), 0, stream, Wc, Err,
-                       U, d_out, d_in, b0, codes, scales, zeros, loss_rows, n_groups);
-    const int kb = (int)std::min<int64_t>(QB, d_in - b0);
-    const int64_t n0 = b0 + kb;
-    if (n0 < d_in) {
-      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - n0, 128);
-      hipLaunchKernelGGL(trailing_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, Wc,
-                         (const float*)Err, U, d_out, d_in, b0, kb, n0);
-    }
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-template <int BITS, bool SYM>
-hipError_t dispatch_g(int group_size, float* Wc, float* Err, const float* U, int64_t d_out,
-                      int64_t d_in, uint8_t* codes, float* scales, float* zeros,
-                      float* loss_rows, int n_groups, hipStream_t s) {
-  switch (group_size) {
-    case 32: return run_quant<BITS, 32, SYM>(Wc, Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, s);
-    case 64: return run_quant<BITS, 64, SYM>(Wc, Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, s);
-    case 128: return run_quant<BITS, 128, SYM>(Wc, Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, s);
-    default: return run_quant<BITS, 0, SYM>(Wc, Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, s);
-  }
+  TrailTile::mma(lds, acc);
+  TrailTile::store<true>(Wc + m0 * d_in + n0t, d_in, rows, cols, acc);
 }
 
 // ---- pack -------------------------------------------------------------------
@@ -439,22 +356,31 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
   const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
   hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out, d_in,
                      dead, w.Wc);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int n_groups = (group_size == -1) ? 1 : (int)(d_in / group_size);
-  const int g = (group_size == -1) ? 0 : group_size;
-  if (sym) {
-    switch (bits) {
-      case 2: return dispatch_g<2, true>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
-      case 3: return dispatch_g<3, true>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
-      default: return dispatch_g<4, true>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
+  QSpec q;
+  q.maxq = (1 << bits) - 1;
+  q.sym = sym ? 1 : 0;
+  q.gsize = (group_size == -1) ? 0 : group_size;
+  q.gshift = 0;
+  while (q.gsize && (1 << q.gshift) < q.gsize) ++q.gshift;
+  q.n_groups = (group_size == -1) ? 1 : (int)(d_in / group_size);
+  if (q.gsize == 0)
+    hipLaunchKernelGGL(rowparams_kernel, dim3((unsigned)ceil_div(d_out, 4)), dim3(256), 0, stream,
+                       (const float*)w.Wc, d_out, d_in, q, scales, zeros);
+  const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
+  for (int64_t b0 = 0; b0 < d_in; b0 += QB) {
+    hipLaunchKernelGGL(colloop_kernel, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err, U, d_out,
+                       d_in, b0, q, codes, scales, zeros, loss_rows);
+    const int kb = (int)std::min<int64_t>(QB, d_in - b0);
+    const int64_t n0 = b0 + kb;
+    if (n0 < d_in) {
+      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - n0, 128);
+      hipLaunchKernelGGL(trailing_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
+                         (const float*)w.Err, U, d_out, d_in, b0, kb, n0);
     }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  switch (bits) {
-    case 2: return dispatch_g<2, false>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
-    case 3: return dispatch_g<3, false>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
-    default: return dispatch_g<4, false>(g, w.Wc, w.Err, U, d_out, d_in, codes, scales, zeros, loss_rows, n_groups, stream);
-  }
+  return hipGetLastError();
 }
 
 hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* zeros,
