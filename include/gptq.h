@@ -62,7 +62,9 @@ typedef void* gptq_stream;
  *          are used.  bf16 values are widened exactly; products are formed
  *          exactly in float32 and summed in float32.
  * n_tokens >= 0 (0 is a no-op); ldx >= d; d >= 1.
- * ws       scratch of gptq_hessian_workspace(d, n_tokens, x_dtype) bytes.
+ * ws       device scratch of gptq_hessian_workspace(d, n_tokens, x_dtype) bytes,
+ *          256-byte aligned; its contents on entry do not matter (it holds the
+ *          split-K partial tiles, which depend on d, n_tokens and x_dtype).
  * The result is deterministic: the same inputs give the same bits.
  * ------------------------------------------------------------------------- */
 int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype,

@@ -13,10 +13,10 @@ struct SyrkPlan {
   int tile;        // output tile edge (256 for bf16, 64 for fp32)
   int ntile;       // tiles per dimension
   int ntri;        // lower-triangle tiles
-  int splits;      // token splits (multiple of 8)
+  int splits;      // token splits (split-K)
   int64_t kper;    // tokens per split
-  size_t partial_bytes; // split-K partial tiles
-  size_t ws_bytes;      // partials + per-tile arrival counters
+  size_t partial_bytes; // split-K partial tiles [splits][ntri][tile * tile] fp32
+  size_t ws_bytes;      // = partial_bytes
 };
 SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype);
 hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n, int64_t ldx,

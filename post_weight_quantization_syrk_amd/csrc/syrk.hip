@@ -2,20 +2,21 @@
 // 阶段一: the layer Hessian is 2 X^T X over the calibration tokens).
 //
 // bf16 inputs: an MFMA SYRK on gfx950.  Each workgroup (4 waves) owns one
-// 256 x 256 lower-triangle tile of H and one contiguous token range (split-K);
-// X tiles are staged through LDS in their natural token-major layout and fed
-// to v_mfma_f32_32x32x16_bf16 through LDS transpose reads
+// 256 x 256 lower-triangle tile of H and one contiguous token range (split-K).
+// X stages go straight from global memory into LDS (global_load_lds, 16 bytes
+// per lane, no staging registers) in their natural token-major layout and are
+// fed to v_mfma_f32_32x32x16_bf16 through LDS transpose reads
 // (ds_read_b64_tr_b16), which deliver each lane 8 consecutive tokens of one
 // column.  bf16 x bf16 products are exact in fp32; sums are fp32.
-// Each token range (split) is pinned to one XCD: its X rows are fetched by that
-// XCD only and shared through its L2 by the tiles resident there.
-// Partial tiles go to a workspace; the last workgroup to finish a tile adds its
-// partials to H in a fixed order, so results are deterministic.
+// Every workgroup writes its partial tile to a workspace; a second kernel adds
+// the partials of each tile to H in split order, so results are deterministic
+// and no workgroup waits on another.
 //
 // fp32 inputs: a plain LDS-tiled fp32 FMA kernel (64 x 64 tiles) with the same
 // split-K / reduction structure.
 #include "common.h"
 #include "kernels.h"
+#include "mfma_f32.h"
 
 #include <algorithm>
 #include <cmath>
@@ -26,10 +27,7 @@ namespace gptq {
 namespace {
 
 constexpr int TB = 256;          // bf16 output tile edge
-constexpr int BK = 64;           // tokens per pipeline stage
-constexpr int PITCH = 288;       // LDS row pitch in bf16 elements (256 + 32)
 constexpr int NTHR = 256;        // 4 waves
-constexpr int BUF = BK * PITCH;  // elements per operand buffer
 
 constexpr int TF = 64;           // fp32 output tile edge
 constexpr int BKF = 32;          // fp32 tokens per stage
@@ -49,237 +47,90 @@ struct SyrkArgs {
   int d;
   int ntri;
   int splits;
+  int vec;          // X rows 16-byte aligned (direct loads allowed)
   int64_t kper;
-  float* partial;
-  unsigned int* counters;  // one per tile, zero on entry, left zero on exit
-  float* H;
+  float* partial;   // [splits][ntri][TB * TB]
 };
 
-// Split-K epilogue shared by both kernels.  Every workgroup has written its
-// partial tile; the last one to arrive for a tile (device-scope counter) adds
-// the partials to H in the fixed order s = 0..S-1, so the result does not
-// depend on which workgroup finishes last.
-template <int TILE, int NT>
-__device__ __forceinline__ void splitk_finish(float* __restrict__ H, int d,
-                                              const float* __restrict__ partial, int ntri,
-                                              int splits, unsigned int* counters, int tile,
-                                              int ti, int tj) {
-  __shared__ unsigned int last_s;
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int old = atomicAdd(&counters[tile], 1u);
-    last_s = (old == (unsigned int)(splits - 1)) ? 1u : 0u;
-  }
-  __syncthreads();
-  if (!last_s) return;
-  __threadfence();
-  constexpr int64_t TSZ = (int64_t)TILE * TILE;
-  const float4* base = (const float4*)(partial + (size_t)tile * TSZ);
-  const size_t sstride = (size_t)ntri * (TSZ / 4);
-  constexpr int PER = 4;  // float4 chunks per thread per pass, loads issued together
-  for (int e0 = threadIdx.x; e0 < TSZ / 4; e0 += NT * PER) {
-    float4 sum[PER];
-    float hv[PER][4];
-    int gi[PER], gj0[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e4 = e0 + u * NT;
-      const int r = (4 * e4) / TILE, c0 = (4 * e4) % TILE;
-      gi[u] = ti * TILE + r;
-      gj0[u] = tj * TILE + c0;
-      sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-      const bool live = e4 < TSZ / 4 && gi[u] < d && gj0[u] < d && gj0[u] <= gi[u];
-      if (!live) gi[u] = -1;
-    }
-    for (int k = 0; k < splits; ++k) {
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        if (gi[u] < 0) continue;
-        const float4 v = base[(size_t)k * sstride + e0 + u * NT];
-        sum[u].x += v.x;
-        sum[u].y += v.y;
-        sum[u].z += v.z;
-        sum[u].w += v.w;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      if (gi[u] < 0) continue;
-      const float* h = H + (int64_t)gi[u] * d + gj0[u];
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        hv[u][q] = (gj0[u] + q < d && gj0[u] + q <= gi[u]) ? h[q] : 0.0f;
-    }
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      if (gi[u] < 0) continue;
-      float* h = H + (int64_t)gi[u] * d + gj0[u];
-      const float vals[4] = {sum[u].x, sum[u].y, sum[u].z, sum[u].w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (gj0[u] + q < d && gj0[u] + q <= gi[u]) h[q] = hv[u][q] + 2.0f * vals[q];
-    }
-  }
-  if (threadIdx.x == 0) counters[tile] = 0u;
-}
-
-__global__ void clear_counters_kernel(unsigned int* c, int n) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) c[i] = 0u;
-}
-
-template <bool VEC>
-__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ X, int64_t ldx, int64_t k0,
-                                          int64_t kend, int c0, int d, int tid, uint4 (&reg)[8]) {
-  const int col = c0 + (tid & 31) * 8;
-  if (VEC && k0 + BK <= kend && c0 + TB <= d) {
-    // Whole stage inside the matrix (the common case): eight unconditional
-    // 16-byte loads, all in flight together.
-    const uint16_t* src = X + (k0 + (tid >> 5)) * ldx + col;
-#pragma unroll
-    for (int r = 0; r < 8; ++r) reg[r] = *(const uint4*)(src + (int64_t)r * 8 * ldx);
-    return;
-  }
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int64_t row = k0 + r * 8 + (tid >> 5);
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (row < kend) {
-      const uint16_t* src = X + row * ldx + col;
-      if (VEC && col + 8 <= d) {
-        v = *(const uint4*)src;
-      } else {
-        uint32_t w[4] = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 8; ++e)
-          if (col + e < d) w[e >> 1] |= ((uint32_t)src[e]) << (16 * (e & 1));
-        v = make_uint4(w[0], w[1], w[2], w[3]);
-      }
-    }
-    reg[r] = v;
-  }
-}
-
-__device__ __forceinline__ void store_rows(uint16_t* buf, int tid, const uint4 (&reg)[8]) {
-  const int vec = tid & 31;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int row = r * 8 + (tid >> 5);
-    *(uint4*)(buf + row * PITCH + vec * 8) = reg[r];
-  }
-}
-
-__device__ __forceinline__ bf16x8 frag(const uint16_t* p) {
-  s16x4 lo = lds_read_tr16(p);
-  s16x4 hi = lds_read_tr16(p + 4 * PITCH);
-  typedef __attribute__((ext_vector_type(8))) short s16x8;
-  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, v);
-}
-
-template <bool VEC>
-__global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * BUF];
-
-  // Workgroups are handed to the 8 XCDs round-robin, so consecutive ids are on
-  // different XCDs.  Token range `split` is pinned to XCD split % 8: every X
-  // row is fetched by one XCD only, and the tiles resident on that XCD stream
-  // the same rows through its L2 at about the same time.
-  const int xcd = blockIdx.x & 7;
-  const int jj = blockIdx.x >> 3;
-  const int tile = jj % a.ntri;
-  const int split = (jj / a.ntri) * 8 + xcd;
+// H(lower) += 2 * sum over splits of the partial tiles, in split order.
+// One workgroup covers 1024 float4 of one tile; each thread keeps 4 float4
+// sums and issues the loads of 4 splits (16 loads) before it adds.
+template <int TILE>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(float* __restrict__ H, int d,
+                                                            const float* __restrict__ partial,
+                                                            int ntri, int splits) {
+  constexpr int F4 = TILE * TILE / 4;   // float4 per tile
+  constexpr int PER_BLOCK = 1024;       // float4 per workgroup
+  constexpr int BLOCKS = F4 / PER_BLOCK;
+  static_assert(F4 % PER_BLOCK == 0, "tile size");
+  const int tile = blockIdx.x / BLOCKS;
+  const int part = blockIdx.x % BLOCKS;
   int ti, tj;
   tri_coords(tile, ti, tj);
-  const bool diag = (ti == tj);
-  const int ci = ti * TB, cj = tj * TB;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int g = lane >> 4, i16 = lane & 15;
-  const int lane_off = (8 * (g >> 1) + (i16 >> 2)) * PITCH + 16 * (g & 1) + 4 * (i16 & 3);
-
-  const int64_t kb = (int64_t)split * a.kper;
-  const int64_t ke = min(a.n, kb + a.kper);
-  const int nst = (ke > kb) ? (int)ceil_div(ke - kb, BK) : 0;
-
-  f32x16 acc[4][4];
+  const float4* base = (const float4*)partial + (size_t)tile * F4 + part * PER_BLOCK + threadIdx.x;
+  const size_t sstride = (size_t)ntri * F4;
+  float4 sum[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int u = 0; u < 4; ++u) sum[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+  int k = 0;
+  for (; k + 4 <= splits; k += 4) {
+    float4 v[4][4];
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  // One register stage in flight: stage s+1 is fetched into registers while
-  // stage s is multiplied out of LDS, then written to the other LDS buffer.
-  // (A second register stage does not fit beside the 256 accumulator
-  // registers without spilling.)
-  uint4 ra[8], rb[8];
-  if (nst > 0) {
-    load_rows<VEC>(a.X, a.ldx, kb, ke, ci, a.d, tid, ra);
-    if (!diag) load_rows<VEC>(a.X, a.ldx, kb, ke, cj, a.d, tid, rb);
-    store_rows(lds, tid, ra);
-    if (!diag) store_rows(lds + BUF, tid, rb);
-    __syncthreads();
-  }
-  for (int s = 0; s < nst; ++s) {
-    const bool more = (s + 1 < nst);
-    if (more) {
-      const int64_t k1 = kb + (int64_t)(s + 1) * BK;
-      load_rows<VEC>(a.X, a.ldx, k1, ke, ci, a.d, tid, ra);
-      if (!diag) load_rows<VEC>(a.X, a.ldx, k1, ke, cj, a.d, tid, rb);
-    }
-    const uint16_t* bufA = lds + (s & 1) * 2 * BUF;
-    const uint16_t* bufB = diag ? bufA : bufA + BUF;
+      for (int u = 0; u < 4; ++u) v[kk][u] = base[(size_t)(k + kk) * sstride + u * 256];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 fa[4], fb[4];
+    for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        fa[mi] = frag(bufA + lane_off + kk * 16 * PITCH + 128 * wm + 32 * mi);
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-        fb[ni] = frag(bufB + lane_off + kk * 16 * PITCH + 128 * wn + 32 * ni);
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* nb = lds + ((s + 1) & 1) * 2 * BUF;
-      store_rows(nb, tid, ra);
-      if (!diag) store_rows(nb + BUF, tid, rb);
-    }
-    __syncthreads();
-  }
-
-  float* out = a.partial + ((size_t)split * a.ntri + tile) * (size_t)(TB * TB);
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int col = 128 * wn + 32 * ni + (lane & 31);
-        out[row * TB + col] = acc[mi][ni][r];
+      for (int u = 0; u < 4; ++u) {
+        sum[u].x += v[kk][u].x;
+        sum[u].y += v[kk][u].y;
+        sum[u].z += v[kk][u].z;
+        sum[u].w += v[kk][u].w;
       }
-  splitk_finish<TB, NTHR>(a.H, a.d, a.partial, a.ntri, a.splits, a.counters, tile, ti, tj);
+  }
+  for (; k < splits; ++k) {
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = base[(size_t)k * sstride + u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sum[u].x += v[u].x;
+      sum[u].y += v[u].y;
+      sum[u].z += v[u].z;
+      sum[u].w += v[u].w;
+    }
+  }
+  float hv[4][4];
+  int gi[4], gj0[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e4 = part * PER_BLOCK + u * 256 + threadIdx.x;
+    gi[u] = ti * TILE + (4 * e4) / TILE;
+    gj0[u] = tj * TILE + (4 * e4) % TILE;
+    const float* h = H + (int64_t)gi[u] * d + gj0[u];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      hv[u][q] = (gi[u] < d && gj0[u] + q < d && gj0[u] + q <= gi[u]) ? h[q] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float* h = H + (int64_t)gi[u] * d + gj0[u];
+    const float vals[4] = {sum[u].x, sum[u].y, sum[u].z, sum[u].w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (gi[u] < d && gj0[u] + q < d && gj0[u] + q <= gi[u]) h[q] = hv[u][q] + 2.0f * vals[q];
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Pipelined variant: X stages go straight from global memory into LDS
-// (global_load_lds, 16 bytes per lane) with no staging registers, four LDS
-// stages of 32 tokens, loads issued four stages ahead; each wave keeps one
-// stage of MFMA fragments in registers and reads the next stage's fragments
-// while it multiplies.  Rows are stored
-// unpadded (512 B) with their 16-byte units XOR-swizzled by 4*(row % 4) so the
+// bf16 SYRK main loop: four LDS stages of 32 tokens, loads issued four stages
+// ahead; each wave keeps one stage of MFMA fragments in registers and reads
+// the next stage's fragments while it multiplies.  Rows are stored unpadded
+// (512 B) with their 16-byte units XOR-swizzled by 4*(row % 4) so the
 // transpose reads of four consecutive rows fall in four different bank
-// groups.  Tiles that overhang the matrix and a partial last stage take a
-// masked register path that writes the same layout.
+// groups.  Tiles that overhang the matrix, unaligned X and a partial last
+// stage take a masked register path that writes the same layout.
 // ---------------------------------------------------------------------------
 constexpr int ABK = 32;                  // tokens per stage
 constexpr int ANS = 4;                   // LDS stages
@@ -317,18 +168,21 @@ __device__ __forceinline__ void dma16(const void* src, char* lds) {
                    : "memory", "m0");
 }
 
-// One operand of one stage.  Wave w fills rows 8w..8w+7 (two rows per 1 KiB
-// wave load); lane l covers row r0 + l/32, physical unit l%32.
+// One operand of one stage.  Wave w fills rows 8w..8w+7 with four 1 KiB
+// wave loads of two rows each (q = 0..3); lane l covers row r0 + l/32,
+// physical unit l%32.
+__device__ __forceinline__ void async_rows(char* buf, const uint16_t* __restrict__ X, int64_t ldx,
+                                           int64_t k0, int c0, int wave, int lane, int q) {
+  const int r0 = 8 * wave + 2 * q;
+  const int row = r0 + (lane >> 5);
+  const int unit = swz_unit(row, lane & 31);
+  const uint16_t* src = X + (k0 + row) * ldx + c0 + 8 * unit;
+  dma16(src, buf + r0 * AROW);
+}
 __device__ __forceinline__ void async_fill(char* buf, const uint16_t* __restrict__ X, int64_t ldx,
                                            int64_t k0, int c0, int wave, int lane) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = 8 * wave + 2 * q;
-    const int row = r0 + (lane >> 5);
-    const int unit = swz_unit(row, lane & 31);
-    const uint16_t* src = X + (k0 + row) * ldx + c0 + 8 * unit;
-    dma16(src, buf + r0 * AROW);
-  }
+  for (int q = 0; q < 4; ++q) async_rows(buf, X, ldx, k0, c0, wave, lane, q);
 }
 
 // Masked path (tile overhanging the matrix, or a partial stage): same layout.
@@ -376,18 +230,20 @@ struct StageFrags {
   bf16x8 b[ABK / 16][4];
 };
 
-__global__ __launch_bounds__(NTHR, 1) void syrk_bf16_async_kernel(SyrkArgs a) {
+__global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[ANS * ASTAGE];
 
-  const int xcd = blockIdx.x & 7;
-  const int jj = blockIdx.x >> 3;
-  const int tile = jj % a.ntri;
-  const int split = (jj / a.ntri) * 8 + xcd;
+  // Split-major order: the workgroups resident at any time (about one per
+  // CU) cover all tiles of one or two token ranges, so every XCD streams the
+  // same X rows at about the same time and its L2 misses for them are
+  // served by the shared last-level cache rather than by HBM, once each.
+  const int tile = blockIdx.x % a.ntri;
+  const int split = blockIdx.x / a.ntri;
   int ti, tj;
   tri_coords(tile, ti, tj);
   const bool diag = (ti == tj);
   const int ci = ti * TB, cj = tj * TB;
-  const bool full_tile = (ci + TB <= a.d) && (cj + TB <= a.d);
+  const bool full_tile = a.vec && (ci + TB <= a.d) && (cj + TB <= a.d);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -437,30 +293,51 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_async_kernel(SyrkArgs a) {
         f.b[kk][ni] = afrag(bufB, kk * 16 + frow, 128 * wn + 32 * ni + fcol);
     }
   };
-  // One stage: publish stage s+1, start loading stage s+ANS into the buffer
-  // stage s occupied (its fragments are already in registers), then run the
-  // 32 MFMAs of stage s interleaved one-to-one with the 32 LDS reads that
-  // fetch stage s+1's fragments.
+  // One stage: publish stage s+1, then run the 32 MFMAs of stage s in four
+  // groups of 8.  Each group is interleaved one-to-one with 8 of the LDS
+  // reads that fetch stage s+1's fragments, and is preceded by one quarter of
+  // the direct loads of stage s+ANS (into the buffer stage s occupied; its
+  // fragments are already in registers).  Spreading the loads keeps the
+  // in-order issue of each wave from stalling on a burst of memory
+  // instructions while the matrix cores sit idle.
   auto step = [&](int s, const StageFrags& cur, StageFrags& nxt) __attribute__((always_inline)) {
     wait_vm(loads_of(s + 2) + loads_of(s + 3));  // own part of stage s+1 landed
     __syncthreads();  // everyone's part landed; every read of stage s's buffer done
-    if (s + ANS < nst) issue(s + ANS);
-    read_stage(min(s + 1, nst - 1), nxt);
+    const int tn = s + ANS;
+    const bool dma = tn < nst && stage_async(tn);
+    if (tn < nst && !dma) issue(tn);  // masked register path
+    char* nbuf = lds + (tn % ANS) * ASTAGE;
+    const int64_t nk0 = kb + (int64_t)tn * ABK;
+    const char* rA = lds + (min(s + 1, nst - 1) % ANS) * ASTAGE;
+    const char* rB = diag ? rA : rA + AOP;
+    StaticFor<0, 4>::run([&](auto G) __attribute__((always_inline)) {
+      constexpr int g = decltype(G)::value;
+      constexpr int kk = g >> 1;
+      if (dma) {
+        async_rows(nbuf, a.X, a.ldx, nk0, ci, wave, lane, g);
+        if (!diag) async_rows(nbuf + AOP, a.X, a.ldx, nk0, cj, wave, lane, g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kk = 0; kk < ABK / 16; ++kk)
+      for (int i = 0; i < 4; ++i) {
+        if constexpr ((g & 1) == 0)
+          nxt.a[kk][i] = afrag(rA, kk * 16 + frow, 128 * wm + 32 * i + fcol);
+        else
+          nxt.b[kk][i] = afrag(rB, kk * 16 + frow, 128 * wn + 32 * i + fcol);
+      }
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int mi = 2 * (g & 1); mi < 2 * (g & 1) + 2; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][mi], cur.b[kk][ni],
                                                                acc[mi][ni], 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 2 * (ABK / 16) * 16; i += 2) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
+      for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   for (int t = 0; t < ANS && t < nst; ++t) issue(t);
@@ -486,9 +363,8 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_async_kernel(SyrkArgs a) {
       for (int r = 0; r < 16; ++r) {
         const int row = 128 * wm + 32 * mi + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int col = 128 * wn + 32 * ni + (lane & 31);
-        out[row * TB + col] = acc[mi][ni][r];
+        __builtin_nontemporal_store(acc[mi][ni][r], out + row * TB + col);
       }
-  splitk_finish<TB, NTHR>(a.H, a.d, a.partial, a.ntri, a.splits, a.counters, tile, ti, tj);
 }
 
 // fp32 inputs: 64 x 64 tile per workgroup, 256 threads x (4 x 4) outputs.
@@ -501,21 +377,13 @@ struct SyrkF32Args {
   int splits;
   int64_t kper;
   float* partial;
-  unsigned int* counters;
-  float* H;
 };
 
 __global__ __launch_bounds__(256) void syrk_f32_kernel(SyrkF32Args a) {
   __shared__ float sa[BKF][TF + 4];
   __shared__ float sb[BKF][TF + 4];
-  // Workgroups are handed to the 8 XCDs round-robin, so consecutive ids are on
-  // different XCDs.  Token range `split` is pinned to XCD split % 8: every X
-  // row is fetched by one XCD only, and the tiles resident on that XCD stream
-  // the same rows through its L2 at about the same time.
-  const int xcd = blockIdx.x & 7;
-  const int jj = blockIdx.x >> 3;
-  const int tile = jj % a.ntri;
-  const int split = (jj / a.ntri) * 8 + xcd;
+  const int tile = blockIdx.x % a.ntri;  // split-major, as for bf16
+  const int split = blockIdx.x / a.ntri;
   int ti, tj;
   tri_coords(tile, ti, tj);
   const int ci = ti * TF, cj = tj * TF;
@@ -558,35 +426,45 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(SyrkF32Args a) {
   for (int p = 0; p < 4; ++p)
 #pragma unroll
     for (int q = 0; q < 4; ++q) out[(ty * 4 + p) * TF + tx * 4 + q] = acc[p][q];
-  splitk_finish<TF, 256>(a.H, a.d, a.partial, a.ntri, a.splits, a.counters, tile, ti, tj);
 }
 
+
 }  // namespace
+
+// Split count: the grid is splits x ntri workgroups, about one resident per
+// CU (128 KiB of LDS each), so it runs in ceil(splits * ntri / 256) rounds of
+// ceil(n / splits / 32) stages.  Pick the split count that minimises rounds x
+// stages plus the cost of writing and re-reading one partial tile per
+// workgroup (about 0.14 stage times each, from the measured stage time and
+// HBM rate), keeping every split at least four stages long.
+static int pick_splits(int64_t n, int ntri, int stage, double partial_cost) {
+  const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(64, n / (4 * stage)));
+  int best = 1;
+  double best_cost = 0.0;
+  for (int s = 1; s <= max_s; ++s) {
+    const double rounds = (double)ceil_div((int64_t)ntri * s, 256);
+    const double stages = (double)ceil_div(ceil_div(n, (int64_t)s), (int64_t)stage);
+    const double cost = rounds * stages + partial_cost * s * ntri;
+    if (s == 1 || cost < best_cost) {
+      best = s;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
 
 SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype) {
   SyrkPlan p{};
   p.tile = (x_dtype == 0) ? TB : TF;
   p.ntile = (int)ceil_div(d, p.tile);
   p.ntri = p.ntile * (p.ntile + 1) / 2;
-  const int bk = (x_dtype == 0) ? BK : BKF;
-  // Split the tokens so that the grid covers the 256 CUs about 4 times over
-  // (one workgroup per CU; a fractional last wave then costs little), but
-  // keep each split at least 4 pipeline stages long.  More splits cost more
-  // partial-tile traffic than they gain in balance (measured at d = 4096).
-  int splits = 8;
-  const char* env = getenv("GPTQ_SYRK_SPLITS");
-  if (env && atoi(env) > 0) {
-    splits = std::max(8, (atoi(env) + 7) / 8 * 8);
-  } else {
-    while (splits < 64 && (int64_t)p.ntri * splits < 4 * 256 &&
-           n / (2 * splits) >= 4 * bk)
-      splits *= 2;
-  }
-  p.splits = splits;
-  p.kper = std::max<int64_t>(bk, ceil_div(ceil_div(std::max<int64_t>(n, 1), splits), bk) * bk);
+  const int bk = (x_dtype == 0) ? ABK : BKF;
+  // fp32 tiles are small (many workgroups per CU): weigh partials lightly.
+  p.splits = pick_splits(std::max<int64_t>(n, 1), p.ntri, bk, (x_dtype == 0) ? 0.14 : 0.01);
+  p.kper = std::max<int64_t>(bk, ceil_div(ceil_div(std::max<int64_t>(n, 1), p.splits), bk) * bk);
   p.partial_bytes = ((size_t)p.splits * p.ntri * (size_t)p.tile * p.tile * sizeof(float) + 255) &
                     ~(size_t)255;
-  p.ws_bytes = p.partial_bytes + (((size_t)p.ntri * sizeof(unsigned int) + 255) & ~(size_t)255);
+  p.ws_bytes = p.partial_bytes;
   return p;
 }
 
@@ -594,26 +472,18 @@ hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t 
                        void* ws, const SyrkPlan& plan, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   float* partial = (float*)ws;
-  unsigned int* counters = (unsigned int*)((char*)ws + plan.partial_bytes);
-  hipLaunchKernelGGL(clear_counters_kernel, dim3((unsigned)ceil_div(plan.ntri, 256)), dim3(256), 0,
-                     stream, counters, plan.ntri);
   const int grid = plan.ntri * plan.splits;
   if (x_dtype == 0) {
-    SyrkArgs a{(const uint16_t*)X, ldx, n, (int)d, plan.ntri, plan.splits, plan.kper, partial,
-               counters, H};
-    const bool vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
-    const char* kenv = getenv("GPTQ_SYRK_KERNEL");  // "staged": register-staged variant
-    const bool staged = kenv && kenv[0] == 's';
-    if (vec && !staged)
-      hipLaunchKernelGGL(syrk_bf16_async_kernel, dim3(grid), dim3(NTHR), 0, stream, a);
-    else if (vec)
-      hipLaunchKernelGGL(syrk_bf16_kernel<true>, dim3(grid), dim3(NTHR), 0, stream, a);
-    else
-      hipLaunchKernelGGL(syrk_bf16_kernel<false>, dim3(grid), dim3(NTHR), 0, stream, a);
+    const int vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
+    SyrkArgs a{(const uint16_t*)X, ldx, n, (int)d, plan.ntri, plan.splits, vec, plan.kper, partial};
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3(grid), dim3(NTHR), 0, stream, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<TB>, dim3(plan.ntri * (TB * TB / 4 / 1024)), dim3(256),
+                       0, stream, H, (int)d, partial, plan.ntri, plan.splits);
   } else {
-    SyrkF32Args a{(const float*)X, ldx, n, (int)d, plan.ntri, plan.splits, plan.kper, partial,
-                  counters, H};
+    SyrkF32Args a{(const float*)X, ldx, n, (int)d, plan.ntri, plan.splits, plan.kper, partial};
     hipLaunchKernelGGL(syrk_f32_kernel, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(splitk_reduce_kernel<TF>, dim3(plan.ntri * (TF * TF / 4 / 1024)), dim3(256),
+                       0, stream, H, (int)d, partial, plan.ntri, plan.splits);
   }
   return hipGetLastError();
 }
