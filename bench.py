@@ -38,8 +38,10 @@ def kernel_source_hash() -> str:
 
 
 def traffic_from_profile():
-    """HBM bytes per SYRK launch from the committed PMC summary, if it was
-    taken on the current kernel source (else None)."""
+    """HBM-side bytes of one Hessian accumulation (SYRK + split-K reduction)
+    from the committed counter summary, if it was taken on the current kernel
+    source (else None): FETCH_SIZE x 2 + WRITE_SIZE x 1, the factors that a
+    1 GiB device copy gives for the same counters."""
     p = os.path.join(ROOT, "profiles", "syrk_bf16_attn4096_262144tok_traffic.json")
     try:
         rec = json.load(open(p))
@@ -187,7 +189,7 @@ def main():
     trail_flops = float(d_out) * d_in * (d_in - wl.block)
     syrk_tflops = syrk_flops / (stage_ms["hessian"] / 1e3) / 1e12
     roofline = {
-        "kernel": "syrk_bf16_async_kernel (H += 2 X^T X, incl. fused split-K reduction)",
+        "kernel": "gptq_hessian_accumulate = syrk_bf16_kernel + splitk_reduce_kernel<256> (H += 2 X^T X)",
         "bound": "mfma",
         "achieved": round(syrk_tflops, 2),
         "peak": PEAK_BF16_TFLOPS,
