@@ -75,6 +75,44 @@ struct MfmaTile {
     constexpr int R = QT ? TN : K, C = QT ? K : TN;
     load_block<R, C, QPITCH>(lds + TM * PP, src, ld, rows, cols);
   }
+  // P and Q together with every load of both in flight at once (one memory
+  // round trip; needs (TM*K + K*TN)/256 staging registers per thread).
+  __device__ static void load_pq(float* lds, const float* __restrict__ ps, int64_t pld, int prows,
+                                 int pcols, const float* __restrict__ qs, int64_t qld, int qrows,
+                                 int qcols) {
+    constexpr int NP = TM * K / 256;
+    constexpr int QR = QT ? TN : K, QC = QT ? K : TN;
+    constexpr int NQ = QR * QC / 256;
+    static_assert(TM * K % 256 == 0 && QR * QC % 256 == 0, "block size");
+    float vp[NP], vq[NQ];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / K, c = e % K;
+      const int rc = r < prows ? r : prows - 1, cc = c < pcols ? c : pcols - 1;
+      vp[u] = ps[(int64_t)rc * pld + cc];
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / QC, c = e % QC;
+      const int rc = r < qrows ? r : qrows - 1, cc = c < qcols ? c : qcols - 1;
+      vq[u] = qs[(int64_t)rc * qld + cc];
+    }
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / K, c = e % K;
+      lds[r * PP + c] = (r < prows && c < pcols) ? vp[u] : 0.0f;
+    }
+    float* lq = lds + TM * PP;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / QC, c = e % QC;
+      lq[r * QPITCH + c] = (r < qrows && c < qcols) ? vq[u] : 0.0f;
+    }
+  }
 
   __device__ static void zero(f32x16 (&acc)[FM][FN]) {
 #pragma unroll
@@ -108,9 +146,9 @@ struct MfmaTile {
     }
   }
 
-  // C[row][col] -= acc (or = acc) for rows < rows, cols < cols.  All loads of
-  // C are issued before any store so the read-modify-write is not serialised
-  // on possible aliasing between the stores and later loads.
+  // C[row][col] -= acc (or = acc) for rows < rows, cols < cols (both >= 1).
+  // All loads of C are issued before any store so the read-modify-write is
+  // not serialised on possible aliasing between the stores and later loads.
   template <bool SUB>
   __device__ static void store(float* C, int64_t ld, int rows, int cols,
                                const f32x16 (&acc)[FM][FN]) {
@@ -125,7 +163,10 @@ struct MfmaTile {
         for (int r = 0; r < 16; ++r) {
           const int row = wm * WM + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int col = wn * WN + 32 * b + (lane & 31);
-          old[a][b][r] = (SUB && row < rows && col < cols) ? C[(int64_t)row * ld + col] : 0.0f;
+          // unconditional load from a clamped address: guarded loads would each
+          // wait for their own memory round trip
+          const int rr = row < rows ? row : rows - 1, cc = col < cols ? col : cols - 1;
+          old[a][b][r] = SUB ? C[(int64_t)rr * ld + cc] : 0.0f;
         }
 #pragma unroll
     for (int a = 0; a < FM; ++a)

@@ -302,8 +302,8 @@ __global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc,
   const int cols = (int)min<int64_t>(128, d_in - n0t);
   f32x16 acc[TrailTile::FM][TrailTile::FN];
   TrailTile::zero(acc);
-  TrailTile::load_p(lds, Err + m0 * d_in + b0, d_in, rows, kb);
-  TrailTile::load_q(lds, U + b0 * d_in + n0t, d_in, kb, cols);
+  TrailTile::load_pq(lds, Err + m0 * d_in + b0, d_in, rows, kb, U + b0 * d_in + n0t, d_in, kb,
+                     cols);
   __syncthreads();
   TrailTile::mma(lds, acc);
   TrailTile::store<true>(Wc + m0 * d_in + n0t, d_in, rows, cols, acc);
