@@ -80,6 +80,7 @@ __global__ __launch_bounds__(256) void qinit_kernel(const void* __restrict__ W, 
 
 struct GroupParams {
   float s, inv_s, hs, z;
+  float hs_lo;  // the largest float below hs (s/2)
 };
 
 // Scale and zero from the group's min/max (asymmetric) or max |v| (symmetric).
@@ -108,25 +109,24 @@ __device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi, i
   p.s = (float)s;
   p.inv_s = 1.0f / p.s;
   p.hs = 0.5f * p.s;
+  p.hs_lo = __int_as_float(__float_as_int(p.hs) - 1);  // hs >= 2^-25: a normal float
   p.z = z;
   return p;
 }
 
 // Nearest integer to the exact quotient x/s, ties to even, then code clamp.
-// q0 = rint(x * (1/s)) is within 1 of it; the exact comparisons against
-// (q0 +- 1/2) s (products of <= 12-bit and 11-bit integers: exact in fp32)
-// settle the last unit.
+// q0 = rint(x * (1/s)) is within 1 of it.  r = x - q0 s is exact (q0 s has
+// at most 22 significant bits, and |r| <= s keeps the difference within
+// x's precision), so comparing r with +-s/2 settles the last unit; a tie
+// (|r| = s/2) moves an odd q0 to its even neighbour, which is the same as
+// comparing against the float just below s/2 when q0 is odd.  Selects only:
+// this sits on the column loop's dependency chain.
 __device__ __forceinline__ float quantize_code(float x, const GroupParams& p, float maxq) {
-  float q0 = rintf(x * p.inv_s);
-  q0 = fminf(fmaxf(q0, -2047.0f), 2047.0f);
-  const float up = fmaf(q0, p.s, p.hs);    // (q0 + 1/2) s, exact
-  const float dn = fmaf(q0, p.s, -p.hs);   // (q0 - 1/2) s, exact
-  const bool odd = (((int)q0) & 1) != 0;
-  if (x > up || (x == up && odd))
-    q0 += 1.0f;
-  else if (x < dn || (x == dn && odd))
-    q0 -= 1.0f;
-  return fminf(fmaxf(q0 + p.z, 0.0f), maxq);
+  const float q0 = __builtin_amdgcn_fmed3f(rintf(x * p.inv_s), -2047.0f, 2047.0f);
+  const float t = (((int)q0) & 1) ? p.hs_lo : p.hs;
+  const float r = fmaf(-q0, p.s, x);
+  const float adj = (r > t) ? 1.0f : ((r < -t) ? -1.0f : 0.0f);
+  return __builtin_amdgcn_fmed3f(q0 + adj + p.z, 0.0f, maxq);
 }
 
 // One group per row: parameters from the whole (current = original) row.
@@ -196,18 +196,17 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     for (int i = 0; i < 8; ++i) w[i] = (8 * c + i < bw) ? w[i] : 0.0f;
   }
   // U block: upper triangle only, identity padding past the matrix edge.
-  // 64 elements per thread, loaded in batches of 16 with clamped addresses.
+  // 64 elements per thread, all loads in flight at once (clamped addresses).
+  {
+    float v[QB * QB / 256];
 #pragma unroll
-  for (int b = 0; b < QB * QB / 256; b += 16) {
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = (b + u) * 256 + tid, r = e >> 7, cc = e & 127;
+    for (int u = 0; u < QB * QB / 256; ++u) {
+      const int e = u * 256 + tid, r = e >> 7, cc = e & 127;
       v[u] = U[(b0 + min(r, bw - 1)) * d_in + b0 + min(cc, bw - 1)];
     }
 #pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = (b + u) * 256 + tid, r = e >> 7, cc = e & 127;
+    for (int u = 0; u < QB * QB / 256; ++u) {
+      const int e = u * 256 + tid, r = e >> 7, cc = e & 127;
       us[r * UPITCH + cc] = (r < bw && cc < bw) ? (cc >= r ? v[u] : 0.0f) : (r == cc ? 1.0f : 0.0f);
     }
   }
@@ -220,16 +219,22 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     gp.s = scales[rr];
     gp.inv_s = 1.0f / gp.s;
     gp.hs = 0.5f * gp.s;
+    gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
     gp.z = zeros[rr];
   }
   const int gmask = q.gsize - 1;
   float cr[8], er[8];
   float loss = 0.0f;
+  // U row of the next column, read one column ahead so the LDS latency is off
+  // the dependency chain.
+  float4 un0 = ((const float4*)(us + 8 * c))[0], un1 = ((const float4*)(us + 8 * c))[1];
   // Fully unrolled over the 128 columns: register indices and the DPP source
-  // lane are compile-time constants.
+  // lane are compile-time constants.  Columns past the matrix edge (j >= bw)
+  // run too, on zero weights against identity rows of U: their delta is 0,
+  // so they change nothing, and keeping every column branch-free lets the
+  // LDS reads of later columns be hoisted off the dependency chain.
   StaticFor<0, QB>::run([&](auto J) {
     constexpr int j = decltype(J)::value;
-    if (j >= bw) return;
     if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
       if (q.gsize != 0 && (j & gmask) == 0) {
         const bool mine = (8 * c >= j) && (8 * c < j + q.gsize);
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void colloop_kernel(
         mx = row_max(mx);
         mn = row_min(mn);
         gp = q.sym ? make_params(mx, 0.0f, q.maxq, 1) : make_params(mn, mx, q.maxq, 0);
-        if (c == (j >> 3) && live) {
+        if (c == (j >> 3) && live && j < bw) {
           const int64_t gi = rr * q.n_groups + ((b0 + j) >> q.gshift);
           scales[gi] = gp.s;
           zeros[gi] = gp.z;
@@ -260,8 +265,12 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       cr[j & 7] = code;
       er[j & 7] = delta;
     }
-    const float4* urow = (const float4*)(us + j * UPITCH + 8 * c);
-    const float4 u0 = urow[0], u1 = urow[1];
+    const float4 u0 = un0, u1 = un1;
+    if constexpr (j + 1 < QB) {
+      const float4* urow = (const float4*)(us + (j + 1) * UPITCH + 8 * c);
+      un0 = urow[0];
+      un1 = urow[1];
+    }
     w[0] = fmaf(-delta, u0.x, w[0]);
     w[1] = fmaf(-delta, u0.y, w[1]);
     w[2] = fmaf(-delta, u0.z, w[2]);

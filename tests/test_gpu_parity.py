@@ -208,6 +208,54 @@ def test_identity_hessian_bit_exact_rtn(bits, g, sym, d_out, d_in):
     np.testing.assert_array_equal(out["codes"], ref["codes"])
 
 
+def _tie_rows(bits, sym, d_in, g, seed):
+    """Rows whose groups have exact binary16 steps and values placed exactly on
+    half steps (ties) and one float32 ulp either side of them."""
+    rng = np.random.default_rng(seed)
+    maxq = (1 << bits) - 1
+    steps = [2.0 ** -4, 3.0 / 64, 5.0 / 128, 2.0 ** -7, 7.0 / 256]
+    rows = []
+    for r in range(len(steps) * 2):
+        s = steps[r % len(steps)]
+        row = np.zeros(d_in, np.float32)
+        for g0 in range(0, d_in, g):
+            if sym:
+                amax = maxq * s / 2.0          # fp16(2 amax / maxq) = s exactly
+                lo_k, hi_k = -(maxq + 1) // 2, (maxq - 1) // 2
+                v = [amax]
+            else:
+                z0 = int(rng.integers(0, maxq + 1))
+                lo_k, hi_k = -z0, maxq - z0
+                v = [lo_k * s, hi_k * s]        # range [lo, hi]: step (hi - lo)/maxq = s
+            while len(v) < g:
+                k = int(rng.integers(lo_k, hi_k))
+                t = np.float32((k + 0.5) * s)
+                kind = int(rng.integers(0, 3))
+                if kind == 1:
+                    t = np.nextafter(t, np.float32(np.inf))
+                elif kind == 2:
+                    t = np.nextafter(t, np.float32(-np.inf))
+                v.append(float(t))
+            row[g0:g0 + g] = rng.permutation(np.array(v[:g], np.float32))
+        rows.append(row)
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("bits,sym", [(4, False), (4, True), (3, False), (2, True)])
+def test_rtn_exact_ties(bits, sym):
+    """Quotients exactly at k + 1/2 round to the even code; one ulp away they
+    round to the nearer one (identity Hessian: the result is plain rounding)."""
+    d_in, g = 128, 32
+    W = _tie_rows(bits, sym, d_in, g, seed=bits * 10 + int(sym))
+    print(f"[ties] bits={bits} sym={sym} {W.shape}", flush=True)
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(2 * np.eye(d_in)))
+    out = _gpu_quant(dev_f32(W), U, dead, bits, g, sym)
+    ref = oracle.rtn(W.astype(np.float64), bits=bits, group_size=g, sym=sym)
+    np.testing.assert_array_equal(out["scales"], ref["scales"])
+    np.testing.assert_array_equal(out["zeros"], ref["zeros"])
+    np.testing.assert_array_equal(out["codes"], ref["codes"])
+
+
 @pytest.mark.parametrize("bits,g,sym", QCASES)
 def test_quantize_parity_correlated(bits, g, sym):
     d_out, d_in = 96, 384
