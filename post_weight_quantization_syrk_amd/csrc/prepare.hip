@@ -122,6 +122,7 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
                                                        int32_t* status) {
   if (*status != 0) return;
   __shared__ float tile[NB][NB + 1];
+  __shared__ float mtile[NB][NB + 1];
   // xs[c % 3]: column c of L strictly below the diagonal (zero elsewhere);
   // mrow[c % 2]: row c of L^{-1}; inv_s[c % 3]: 1 / L_cc.
   __shared__ __attribute__((aligned(16))) float xs[3][NB];
@@ -186,6 +187,11 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
 #pragma unroll
       for (int i = 0; i < 16; ++i) a[i] = fmaf(-xr, xc[16 * q + i], a[i]);
     }
+    // Next column first: it is the only work on the step-to-step chain; the
+    // inverse update below overlaps its LDS write and the barrier wait.
+    if constexpr (c + 1 < NB) {
+      if (q == ((c + 1) >> 4)) make_col(std::integral_constant<int, c + 1>{});
+    }
     if constexpr (c > 0) {
       constexpr int qp = (c - 1) >> 4;
       const float xp = xs[(c - 1) % 3][r];
@@ -203,24 +209,43 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
         mrow[c % 2][16 * q + i] = b[i];
       }
     }
-    if constexpr (c + 1 < NB) {
-      if (q == ((c + 1) >> 4)) make_col(std::integral_constant<int, c + 1>{});
-    }
     __syncthreads();
   });
   if (bad_s != 0) {
     if (t == 0) *status = d - (k0 + bad_s - 1);
     return;
   }
+  // Stage L and L^{-1} through LDS so the global stores are row-contiguous
+  // (a thread's own 16 values all sit in one row: 64 rows per store
+  // instruction otherwise).
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int c = 16 * q + i;
-    const float lv = (c <= r) ? a[i] : 0.0f;
-    const float mv = (c <= r) ? b[i] : 0.0f;
-    Dinv[r * NB + c] = mv;
-    if (r < kb && c < kb) {
-      if (c <= r) A[(int64_t)(k0 + r) * d + k0 + c] = lv;
-      M[(int64_t)(k0 + r) * d + k0 + c] = mv;  // zero above the diagonal
+    tile[r][c] = (c <= r) ? a[i] : 0.0f;
+    mtile[r][c] = (c <= r) ? b[i] : 0.0f;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int rr = 16 * u + (t >> 4), c0 = 4 * (t & 15);
+    float lv[4], mv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lv[e] = tile[rr][c0 + e];
+      mv[e] = mtile[rr][c0 + e];
+    }
+    *(float4*)(Dinv + rr * NB + c0) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    if (rr < kb) {
+      float* arow = A + (int64_t)(k0 + rr) * d + k0;
+      float* mrow_g = M + (int64_t)(k0 + rr) * d + k0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = c0 + e;
+        if (c < kb) {
+          if (c <= rr) arow[c] = lv[e];
+          mrow_g[c] = mv[e];  // zero above the diagonal
+        }
+      }
     }
   }
 }
