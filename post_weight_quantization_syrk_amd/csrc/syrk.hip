@@ -124,18 +124,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(float* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// bf16 SYRK main loop: four LDS stages of 32 tokens, loads issued four stages
-// ahead; each wave keeps one stage of MFMA fragments in registers and reads
-// the next stage's fragments while it multiplies.  Rows are stored unpadded
+// bf16 SYRK main loop: three LDS stages of 48 tokens, loads issued three
+// stages ahead; each wave keeps one stage of MFMA fragments in registers and
+// reads the next stage's fragments while it multiplies.  Rows are stored unpadded
 // (512 B) with their 16-byte units XOR-swizzled by 4*(row % 4) so the
 // transpose reads of four consecutive rows fall in four different bank
 // groups.  Tiles that overhang the matrix, unaligned X and a partial last
 // stage take a masked register path that writes the same layout.
 // ---------------------------------------------------------------------------
-constexpr int ABK = 32;                  // tokens per stage
-constexpr int ANS = 4;                   // LDS stages
+constexpr int ABK = 48;                  // tokens per stage
+constexpr int ANS = 3;                   // LDS stages (3 x 48 KiB)
+constexpr int RPW = ABK / 4;             // rows per wave per operand
+constexpr int NQ = RPW / 2;              // direct loads per wave per operand
 constexpr int AROW = TB * 2;             // bytes per LDS row (256 bf16)
-constexpr int AOP = ABK * AROW;          // bytes per operand per stage (16 KiB)
+constexpr int AOP = ABK * AROW;          // bytes per operand per stage (24 KiB)
 constexpr int ASTAGE = 2 * AOP;          // bytes per stage (A and B)
 
 __device__ __forceinline__ int swz_unit(int row, int unit) { return unit ^ (4 * (row & 3)); }
@@ -160,29 +162,49 @@ __device__ __forceinline__ bf16x8 afrag(const char* buf, int row, int col) {
 // (vmcnt(0)) before any LDS read, which serialises the stage pipeline.  The
 // asm has no output registers; completion is awaited explicitly (wait_vm)
 // before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void* src, char* lds) {
-  const uint32_t base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
-  __asm__ volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds_off) {
+  // base and the LDS offset are wave-uniform by construction; readfirstlane
+  // lets the compiler keep them in SGPRs for the "s" operands
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const void* sbase = (const void*)(uintptr_t)(((uint64_t)bhi << 32) | blo);
+  const uint32_t lbase = __builtin_amdgcn_readfirstlane(lds_off);
+  __asm__ volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                    :
-                   : "v"(src), "s"(base)
+                   : "v"(voff), "s"(sbase), "s"(lbase)
                    : "memory", "m0");
 }
 
-// One operand of one stage.  Wave w fills rows 8w..8w+7 with four 1 KiB
-// wave loads of two rows each (q = 0..3); lane l covers row r0 + l/32,
-// physical unit l%32.
-__device__ __forceinline__ void async_rows(char* buf, const uint16_t* __restrict__ X, int64_t ldx,
-                                           int64_t k0, int c0, int wave, int lane, int q) {
-  const int r0 = 8 * wave + 2 * q;
-  const int row = r0 + (lane >> 5);
-  const int unit = swz_unit(row, lane & 31);
-  const uint16_t* src = X + (k0 + row) * ldx + c0 + 8 * unit;
-  dma16(src, buf + r0 * AROW);
-}
-__device__ __forceinline__ void async_fill(char* buf, const uint16_t* __restrict__ X, int64_t ldx,
-                                           int64_t k0, int c0, int wave, int lane) {
+// One operand of one stage.  Wave w fills rows RPW*w .. RPW*w + RPW-1 with
+// wave loads of two rows each (q = 0 .. NQ-1); lane l covers row r0 + l/32,
+// physical unit l%32.  The row pair's start is a wave-uniform base; the
+// per-lane byte offset within the pair depends only on the swizzle phase
+// (q % 2), so two offsets per operand serve every load.
+struct DmaOff {
+  uint32_t v[2];
+};
+__device__ __forceinline__ DmaOff dma_offsets(int64_t ldx, int c0, int lane) {
+  DmaOff o;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) async_rows(buf, X, ldx, k0, c0, wave, lane, q);
+  for (int ph = 0; ph < 2; ++ph) {
+    const int rl = lane >> 5;
+    const int unit = swz_unit(2 * ph + rl, lane & 31);
+    o.v[ph] = (uint32_t)(((int64_t)rl * ldx + c0 + 8 * unit) * 2);
+  }
+  return o;
+}
+// buf: LDS byte offset of the operand buffer.
+__device__ __forceinline__ void async_rows(uint32_t buf, const uint16_t* __restrict__ X,
+                                           int64_t ldx, int64_t k0, const DmaOff& off, int wave,
+                                           int q) {
+  const int r0 = RPW * wave + 2 * q;
+  dma16(X + (k0 + r0) * ldx, off.v[q & 1], buf + (uint32_t)(r0 * AROW));
+}
+__device__ __forceinline__ void async_fill(uint32_t buf, const uint16_t* __restrict__ X,
+                                           int64_t ldx, int64_t k0, const DmaOff& off, int wave) {
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) async_rows(buf, X, ldx, k0, off, wave, q);
 }
 
 // Masked path (tile overhanging the matrix, or a partial stage): same layout.
@@ -190,8 +212,8 @@ __device__ __forceinline__ void masked_fill(char* buf, const uint16_t* __restric
                                             int64_t k0, int64_t kend, int c0, int d, int wave,
                                             int lane) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r0 = 8 * wave + 2 * q;
+  for (int q = 0; q < NQ; ++q) {
+    const int r0 = RPW * wave + 2 * q;
     const int row = r0 + (lane >> 5);
     const int unit = swz_unit(row, lane & 31);
     const int col = c0 + 8 * unit;
@@ -218,6 +240,8 @@ __device__ __forceinline__ void wait_vm(int n) {
     __asm__ volatile("s_waitcnt vmcnt(12)" ::: "memory");
   else if (n >= 8)
     __asm__ volatile("s_waitcnt vmcnt(8)" ::: "memory");
+  else if (n >= 6)
+    __asm__ volatile("s_waitcnt vmcnt(6)" ::: "memory");
   else if (n >= 4)
     __asm__ volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
@@ -232,6 +256,7 @@ struct StageFrags {
 
 __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   __shared__ __attribute__((aligned(1024))) char lds[ANS * ASTAGE];
+  const uint32_t lds_off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 
   // Split-major order: the workgroups resident at any time (about one per
   // CU) cover all tiles of one or two token ranges, so every XCD streams the
@@ -256,15 +281,17 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   const int64_t kb = (int64_t)split * a.kper;
   const int64_t ke = min(a.n, kb + a.kper);
   const int nst = (ke > kb) ? (int)ceil_div(ke - kb, ABK) : 0;
-  const int per_stage = diag ? 4 : 8;  // direct loads per wave per full stage
+  const int per_stage = diag ? NQ : 2 * NQ;  // direct loads per wave per full stage
+  const DmaOff offA = dma_offsets(a.ldx, ci, lane), offB = dma_offsets(a.ldx, cj, lane);
 
-  auto stage_async = [&](int t) { return full_tile && kb + (int64_t)(t + 1) * ABK <= ke; };
-  auto issue = [&](int t) {
+  auto stage_async = [&](int t) __attribute__((always_inline)) { return full_tile && kb + (int64_t)(t + 1) * ABK <= ke; };
+  auto issue = [&](int t) __attribute__((always_inline)) {
     char* buf = lds + (t % ANS) * ASTAGE;
     const int64_t k0 = kb + (int64_t)t * ABK;
     if (stage_async(t)) {
-      async_fill(buf, a.X, a.ldx, k0, ci, wave, lane);
-      if (!diag) async_fill(buf + AOP, a.X, a.ldx, k0, cj, wave, lane);
+      const uint32_t bo = lds_off + (uint32_t)((t % ANS) * ASTAGE);
+      async_fill(bo, a.X, a.ldx, k0, offA, wave);
+      if (!diag) async_fill(bo + AOP, a.X, a.ldx, k0, offB, wave);
     } else {
       masked_fill(buf, a.X, a.ldx, k0, ke, ci, a.d, wave, lane);
       if (!diag) masked_fill(buf + AOP, a.X, a.ldx, k0, ke, cj, a.d, wave, lane);
@@ -279,7 +306,7 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
 
-  auto loads_of = [&](int t) { return (t < nst && stage_async(t)) ? per_stage : 0; };
+  auto loads_of = [&](int t) __attribute__((always_inline)) { return (t < nst && stage_async(t)) ? per_stage : 0; };
   auto read_stage = [&](int t, StageFrags& f) __attribute__((always_inline)) {
     const char* bufA = lds + (t % ANS) * ASTAGE;
     const char* bufB = diag ? bufA : bufA + AOP;
@@ -293,29 +320,32 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
         f.b[kk][ni] = afrag(bufB, kk * 16 + frow, 128 * wn + 32 * ni + fcol);
     }
   };
-  // One stage: publish stage s+1, then run the 32 MFMAs of stage s in four
+  // One stage: publish stage s+1, then run the 48 MFMAs of stage s in six
   // groups of 8.  Each group is interleaved one-to-one with 8 of the LDS
-  // reads that fetch stage s+1's fragments, and is preceded by one quarter of
-  // the direct loads of stage s+ANS (into the buffer stage s occupied; its
-  // fragments are already in registers).  Spreading the loads keeps the
-  // in-order issue of each wave from stalling on a burst of memory
+  // reads that fetch stage s+1's fragments, and is preceded by one of the
+  // six direct loads (per operand) of stage s+ANS, into the buffer stage s
+  // occupied (its fragments are already in registers).  Spreading the loads
+  // keeps the in-order issue of each wave from stalling on a burst of memory
   // instructions while the matrix cores sit idle.
   auto step = [&](int s, const StageFrags& cur, StageFrags& nxt) __attribute__((always_inline)) {
-    wait_vm(loads_of(s + 2) + loads_of(s + 3));  // own part of stage s+1 landed
+    { int later = 0;
+#pragma unroll
+      for (int t = 2; t < ANS; ++t) later += loads_of(s + t);
+      wait_vm(later); }
     __syncthreads();  // everyone's part landed; every read of stage s's buffer done
     const int tn = s + ANS;
     const bool dma = tn < nst && stage_async(tn);
     if (tn < nst && !dma) issue(tn);  // masked register path
-    char* nbuf = lds + (tn % ANS) * ASTAGE;
     const int64_t nk0 = kb + (int64_t)tn * ABK;
     const char* rA = lds + (min(s + 1, nst - 1) % ANS) * ASTAGE;
     const char* rB = diag ? rA : rA + AOP;
-    StaticFor<0, 4>::run([&](auto G) __attribute__((always_inline)) {
+    StaticFor<0, 2 * (ABK / 16)>::run([&](auto G) __attribute__((always_inline)) {
       constexpr int g = decltype(G)::value;
       constexpr int kk = g >> 1;
       if (dma) {
-        async_rows(nbuf, a.X, a.ldx, nk0, ci, wave, lane, g);
-        if (!diag) async_rows(nbuf + AOP, a.X, a.ldx, nk0, cj, wave, lane, g);
+        const uint32_t nbo = lds_off + (uint32_t)((tn % ANS) * ASTAGE);
+        async_rows(nbo, a.X, a.ldx, nk0, offA, wave, g);
+        if (!diag) async_rows(nbo + AOP, a.X, a.ldx, nk0, offB, wave, g);
       }
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -343,7 +373,10 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   for (int t = 0; t < ANS && t < nst; ++t) issue(t);
   StageFrags f0, f1;
   if (nst > 0) {
-    wait_vm(loads_of(1) + loads_of(2) + loads_of(3));
+    { int later = 0;
+#pragma unroll
+      for (int t = 1; t < ANS; ++t) later += loads_of(t);
+      wait_vm(later); }
     __syncthreads();
     read_stage(0, f0);
   }
@@ -432,10 +465,10 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(SyrkF32Args a) {
 }  // namespace
 
 // Split count: the grid is splits x ntri workgroups, about one resident per
-// CU (128 KiB of LDS each), so it runs in ceil(splits * ntri / 256) rounds of
-// ceil(n / splits / 32) stages.  Pick the split count that minimises rounds x
+// CU (144 KiB of LDS each), so it runs in ceil(splits * ntri / 256) rounds of
+// ceil(n / splits / 48) stages.  Pick the split count that minimises rounds x
 // stages plus the cost of writing and re-reading one partial tile per
-// workgroup (about 0.14 stage times each, from the measured stage time and
+// workgroup (about 0.1 stage times each, from the measured stage time and
 // HBM rate), keeping every split at least four stages long.
 static int pick_splits(int64_t n, int ntri, int stage, double partial_cost) {
   const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(64, n / (4 * stage)));
@@ -460,7 +493,7 @@ SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype) {
   p.ntri = p.ntile * (p.ntile + 1) / 2;
   const int bk = (x_dtype == 0) ? ABK : BKF;
   // fp32 tiles are small (many workgroups per CU): weigh partials lightly.
-  p.splits = pick_splits(std::max<int64_t>(n, 1), p.ntri, bk, (x_dtype == 0) ? 0.14 : 0.01);
+  p.splits = pick_splits(std::max<int64_t>(n, 1), p.ntri, bk, (x_dtype == 0) ? 0.1 : 0.01);
   p.kper = std::max<int64_t>(bk, ceil_div(ceil_div(std::max<int64_t>(n, 1), p.splits), bk) * bk);
   p.partial_bytes = ((size_t)p.splits * p.ntri * (size_t)p.tile * p.tile * sizeof(float) + 255) &
                     ~(size_t)255;
@@ -474,7 +507,10 @@ hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t 
   float* partial = (float*)ws;
   const int grid = plan.ntri * plan.splits;
   if (x_dtype == 0) {
-    const int vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0);
+    // direct loads: 16-byte aligned rows, and per-lane byte offsets within a
+    // row pair (< 2 ldx + d elements) that fit the 32-bit offset operand
+    const int vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0) &&
+                    (2 * ldx + d) * 2 < ((int64_t)1 << 31);
     SyrkArgs a{(const uint16_t*)X, ldx, n, (int)d, plan.ntri, plan.splits, vec, plan.kper, partial};
     hipLaunchKernelGGL(syrk_bf16_kernel, dim3(grid), dim3(NTHR), 0, stream, a);
     hipLaunchKernelGGL(splitk_reduce_kernel<TB>, dim3(plan.ntri * (TB * TB / 4 / 1024)), dim3(256),
