@@ -29,4 +29,12 @@ __device__ __forceinline__ s16x4 lds_read_tr16(const void* lds_generic_ptr) {
 
 __host__ __device__ constexpr int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Broadcast lane `SRC` (0..15) of each 16-lane row to the whole row (DPP
+// row_newbcast): a VGPR-to-VGPR move, no scalar register involved.
+template <int SRC>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __int_as_float(
+      __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + SRC, 0xF, 0xF, false));
+}
+
 }  // namespace gptq

@@ -111,26 +111,34 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
   }
 }
 
-// Diagonal block: L_kk = chol(A_kk) and Dinv = L_kk^{-1} by 256 threads; thread
-// (r = t % 64, wave q = t / 64) holds columns 16q..16q+15 of row r.  Column c of
-// L below the diagonal and row c of L^{-1} are exchanged through LDS; all
-// per-element conditions are folded into zeros so the loop has no divergent
-// branches.
+// Diagonal block: L_kk = chol(A_kk) and Dinv = L_kk^{-1}, by 256 threads in
+// four 16-column sub-steps S = [s0, s0 + 16), s0 = 16 s:
+//   A: wave 0 factors the 16 x 16 block A_SS in registers (lane r of each
+//      16-lane row holds row r; pivots and column values are broadcast with
+//      DPP row broadcasts, so the 16 dependent pivot steps need no barrier and
+//      no scalar registers) and inverts it (M_SS);
+//      meanwhile waves 1-3 form R = L_{S,0:s0} M_{0:s0,0:s0}, which the rows
+//      of L^{-1} below need;
+//   B: the panel L_{i,S} = A_{i,S} M_SS^T for rows i below S, and the row
+//      block M_{S,0:s0} = -M_SS R of L^{-1};
+//   C: the rank-16 update A_{i,j} -= L_{i,S} L_{j,S}^T of the rows below S.
+// A failed pivot (not positive or not finite) is replaced by 1 so the
+// factorization finishes with finite values; the first one is reported.
+constexpr int SB = 16;
+constexpr int PP16 = 20;  // LDS pitch (floats) of the 16-wide panel copy: 16-byte rows
+
 __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
                                                        float* __restrict__ M,
                                                        float* __restrict__ Dinv, int d, int k,
                                                        int32_t* status) {
   if (*status != 0) return;
-  __shared__ float tile[NB][NB + 1];
-  __shared__ float mtile[NB][NB + 1];
-  // xs[c % 3]: column c of L strictly below the diagonal (zero elsewhere);
-  // mrow[c % 2]: row c of L^{-1}; inv_s[c % 3]: 1 / L_cc.
-  __shared__ __attribute__((aligned(16))) float xs[3][NB];
-  __shared__ __attribute__((aligned(16))) float mrow[2][NB];
-  __shared__ float inv_s[3];
+  __shared__ float tile[NB][NB + 1];   // A_kk, becomes L_kk (lower)
+  __shared__ float mtile[NB][NB + 1];  // L_kk^{-1} (lower)
+  __shared__ float rbuf[SB][NB + 1];   // R of the current sub-step
+  __shared__ __attribute__((aligned(16))) float pan[NB][PP16];  // panel copy L_{i,S}
   __shared__ int bad_s;
-  const int t = threadIdx.x, r = t & 63;
-  const int q = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int k0 = k * NB;
   const int kb = min(NB, d - k0);
   {
@@ -146,85 +154,138 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
     for (int u = 0; u < 16; ++u) {
       const int e = u * 256 + t, rr = e >> 6, cc = e & 63;
       tile[rr][cc] = (rr < kb && cc < kb) ? ((cc <= rr) ? v[u] : 0.0f) : (rr == cc ? 1.0f : 0.0f);
+      mtile[rr][cc] = 0.0f;
     }
   }
-  __syncthreads();
-  float a[16], b[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    a[i] = tile[r][16 * q + i];
-    b[i] = (r == 16 * q + i) ? 1.0f : 0.0f;
-  }
-  // Column c of L is formed by the wave that owns it, right after that wave has
-  // applied step c-1's update, and published before the step's only barrier.
-  // The update of L^{-1} by column c is applied one step late, just before the
-  // row it completes is needed.
-  auto make_col = [&](auto C) {
-    constexpr int c = decltype(C)::value, ic = c & 15;
-    float piv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[ic]), c));
-    if (!(piv > 0.0f) || !(piv < 3.0e38f)) {  // non-positive, NaN or Inf pivot
-      if (r == 0 && bad_s == 0) bad_s = c + 1;  // keep the first failure
-      piv = 1.0f;
-    }
-    const float inv = __builtin_amdgcn_rsqf(piv);  // 1/sqrt, within 1 ulp
-    const float lc = piv * inv;
-    const float x = a[ic] * inv;
-    xs[c % 3][r] = (r > c) ? x : 0.0f;
-    a[ic] = (r > c) ? x : (r == c ? lc : 0.0f);
-    if (r == 0) inv_s[c % 3] = inv;
-  };
   if (t == 0) bad_s = 0;
   __syncthreads();
-  if (q == 0) make_col(std::integral_constant<int, 0>{});
-  __syncthreads();
-  // A failed pivot is replaced by 1 so the loop runs on with finite values;
-  // the first failure is reported after the loop.
-  StaticFor<0, NB>::run([&](auto C) {
-    constexpr int c = decltype(C)::value, qc = c >> 4;
-    const float* xc = xs[c % 3];
-    const float xr = xc[r];
-    if (q >= qc) {
+
+  StaticFor<0, NB / SB>::run([&](auto Sv) {
+    constexpr int s = decltype(Sv)::value, s0 = SB * s;
+    constexpr int rows = NB - s0 - SB;  // rows below the sub-block
+    // ---------------- A
+    if (wave == 0) {
+      const int r = lane & (SB - 1);  // lanes 16..63 repeat rows 0..15; only 0..15 write
+      float a[SB], m[SB];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) a[i] = fmaf(-xr, xc[16 * q + i], a[i]);
-    }
-    // Next column first: it is the only work on the step-to-step chain; the
-    // inverse update below overlaps its LDS write and the barrier wait.
-    if constexpr (c + 1 < NB) {
-      if (q == ((c + 1) >> 4)) make_col(std::integral_constant<int, c + 1>{});
-    }
-    if constexpr (c > 0) {
-      constexpr int qp = (c - 1) >> 4;
-      const float xp = xs[(c - 1) % 3][r];
-      const float* mp = mrow[(c - 1) % 2];
-      if (q <= qp) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) b[i] = fmaf(-xp, mp[16 * q + i], b[i]);
+      for (int j = 0; j < SB; ++j) {
+        a[j] = (j <= r) ? tile[s0 + r][s0 + j] : 0.0f;
+        m[j] = (j == r) ? 1.0f : 0.0f;
       }
-    }
-    if (r == c) {
-      const float inv = inv_s[c % 3];
+      int bad = 0;
+      StaticFor<0, SB>::run([&](auto Cv) {
+        constexpr int c = decltype(Cv)::value;
+        float piv = row_bcast<c>(a[c]);
+        const bool ok = (piv > 0.0f) && (piv < 3.0e38f);
+        bad = (bad == 0 && !ok) ? (s0 + c + 1) : bad;
+        piv = ok ? piv : 1.0f;
+        const float inv = __builtin_amdgcn_rsqf(piv);  // 1/sqrt, within 1 ulp
+        const float l = (r > c) ? a[c] * inv : 0.0f;   // L[r][c] below the diagonal
+        a[c] = (r > c) ? l : ((r == c) ? piv * inv : 0.0f);
+        StaticFor<c + 1, SB>::run([&](auto Jv) {
+          constexpr int j = decltype(Jv)::value;
+          a[j] = fmaf(-l, row_bcast<j>(l), a[j]);      // only the lower part is used
+        });
+        const float sc = (r == c) ? inv : 1.0f;        // completes row c of L^{-1}
+        StaticFor<0, c + 1>::run([&](auto Qv) {
+          constexpr int q = decltype(Qv)::value;
+          m[q] *= sc;
+          m[q] = fmaf(-l, row_bcast<c>(m[q]), m[q]);   // eliminate below (l = 0 above)
+        });
+      });
+      if (lane < SB) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        b[i] *= inv;
-        mrow[c % 2][16 * q + i] = b[i];
+        for (int j = 0; j < SB; ++j) {
+          tile[s0 + r][s0 + j] = (j <= r) ? a[j] : 0.0f;
+          mtile[s0 + r][s0 + j] = (j <= r) ? m[j] : 0.0f;
+        }
+      }
+      if (lane == 0 && bad != 0) bad_s = (bad_s == 0 || bad < bad_s) ? bad : bad_s;
+    } else if constexpr (s > 0) {
+      // R[r][c] = sum_{m=c}^{s0-1} L[s0+r][m] M[m][c]: thread (c, 4 rows)
+      const int e = t - 64;
+      if (e < 4 * s0) {
+        const int c = e % s0, r0 = 4 * (e / s0);
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int mm = c; mm < s0; ++mm) {
+          const float mv = mtile[mm][c];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(tile[s0 + r0 + i][mm], mv, acc[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rbuf[r0 + i][c] = acc[i];
       }
     }
     __syncthreads();
+    // ---------------- B
+    // Threads [0, 4 rows): panel row i, columns 4jg..4jg+3:
+    //   L[i][s0+j] = sum_{q<=j} A[i][s0+q] M_SS[j][q].
+    // Threads [4 rows, 4 rows + 4 s0): row block of L^{-1}, column c, rows
+    //   4g..4g+3:  M[s0+r][c] = -sum_{p<=r} M_SS[r][p] R[p][c].
+    float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (t < 4 * rows) {
+      const int i = s0 + SB + (t >> 2), j0 = 4 * (t & 3);
+#pragma unroll
+      for (int q = 0; q < SB; ++q) {
+        const float av = tile[i][s0 + q];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (q <= j0 + u) pv[u] = fmaf(av, mtile[s0 + j0 + u][s0 + q], pv[u]);
+      }
+    }
+    if constexpr (s > 0) {
+      if (t >= 4 * rows && t < 4 * rows + 4 * s0) {
+        const int e = t - 4 * rows;
+        const int c = e % s0, g0 = 4 * (e / s0);
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int p = 0; p < SB; ++p) {
+          const float rv = rbuf[p][c];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (p <= g0 + u) acc[u] = fmaf(mtile[s0 + g0 + u][s0 + p], rv, acc[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) mtile[s0 + g0 + u][c] = -acc[u];
+      }
+    }
+    __syncthreads();  // every read of the panel's A values is done
+    if (t < 4 * rows) {
+      const int i = s0 + SB + (t >> 2), j0 = 4 * (t & 3);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tile[i][s0 + j0 + u] = pv[u];
+        pan[i][j0 + u] = pv[u];
+      }
+    }
+    __syncthreads();
+    // ---------------- C
+    if constexpr (rows > 0) {
+      for (int e = t; e < rows * rows; e += 256) {
+        const int i = s0 + SB + e / rows, jj = s0 + SB + e % rows;
+        if (jj <= i) {
+          const float4* pi = (const float4*)pan[i];
+          const float4* pj = (const float4*)pan[jj];
+          float acc = 0.0f;
+#pragma unroll
+          for (int q = 0; q < SB / 4; ++q) {
+            const float4 x = pi[q], y = pj[q];
+            acc = fmaf(x.x, y.x, acc);
+            acc = fmaf(x.y, y.y, acc);
+            acc = fmaf(x.z, y.z, acc);
+            acc = fmaf(x.w, y.w, acc);
+          }
+          tile[i][jj] -= acc;
+        }
+      }
+      __syncthreads();
+    }
   });
   if (bad_s != 0) {
     if (t == 0) *status = d - (k0 + bad_s - 1);
     return;
   }
-  // Stage L and L^{-1} through LDS so the global stores are row-contiguous
-  // (a thread's own 16 values all sit in one row: 64 rows per store
-  // instruction otherwise).
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int c = 16 * q + i;
-    tile[r][c] = (c <= r) ? a[i] : 0.0f;
-    mtile[r][c] = (c <= r) ? b[i] : 0.0f;
-  }
-  __syncthreads();
+  // Global stores, row-contiguous (16 threads per 64-float row).
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int rr = 16 * u + (t >> 4), c0 = 4 * (t & 15);
@@ -232,7 +293,7 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       lv[e] = tile[rr][c0 + e];
-      mv[e] = mtile[rr][c0 + e];
+      mv[e] = (c0 + e <= rr) ? mtile[rr][c0 + e] : 0.0f;
     }
     *(float4*)(Dinv + rr * NB + c0) = make_float4(mv[0], mv[1], mv[2], mv[3]);
     if (rr < kb) {

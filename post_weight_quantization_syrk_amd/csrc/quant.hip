@@ -155,12 +155,6 @@ __global__ __launch_bounds__(256) void rowparams_kernel(const float* __restrict_
   }
 }
 
-// Broadcast lane `SRC` (0..15) of each 16-lane row to the whole row.
-template <int SRC>
-__device__ __forceinline__ float row_bcast(float v) {
-  return __int_as_float(
-      __builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + SRC, 0xF, 0xF, false));
-}
 
 __device__ __forceinline__ float row_min(float v) {
 #pragma unroll
