@@ -154,9 +154,11 @@ struct MfmaTile {
                                const f32x16 (&acc)[FM][FN]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int wm = wave & 1, wn = wave >> 1;
-    float old[FM][FN][16];
+    // One row of MFMA tiles at a time: its loads all in flight, then its
+    // stores (bounds the registers held for the old values).
 #pragma unroll
-    for (int a = 0; a < FM; ++a)
+    for (int a = 0; a < FM; ++a) {
+      float old[FN][16];
 #pragma unroll
       for (int b = 0; b < FN; ++b)
 #pragma unroll
@@ -166,10 +168,8 @@ struct MfmaTile {
           // unconditional load from a clamped address: guarded loads would each
           // wait for their own memory round trip
           const int rr = row < rows ? row : rows - 1, cc = col < cols ? col : cols - 1;
-          old[a][b][r] = SUB ? C[(int64_t)rr * ld + cc] : 0.0f;
+          old[b][r] = SUB ? C[(int64_t)rr * ld + cc] : 0.0f;
         }
-#pragma unroll
-    for (int a = 0; a < FM; ++a)
 #pragma unroll
       for (int b = 0; b < FN; ++b)
 #pragma unroll
@@ -177,8 +177,9 @@ struct MfmaTile {
           const int row = wm * WM + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int col = wn * WN + 32 * b + (lane & 31);
           if (row < rows && col < cols)
-            C[(int64_t)row * ld + col] = SUB ? old[a][b][r] - acc[a][b][r] : acc[a][b][r];
+            C[(int64_t)row * ld + col] = SUB ? old[b][r] - acc[a][b][r] : acc[a][b][r];
         }
+    }
   }
 
   // Visit every accumulator element with its (row, col) inside the tile.

@@ -288,27 +288,35 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]   (fp32 MFMA, 128 x 128 tiles, K = 128)
-using TrailTile = MfmaTile<128, 128, QB, false>;
+// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]   (fp32 MFMA, 128 x 64 tiles).
+// K = 128 runs as two chunks of 64 through 57 KiB of LDS and <= 256 registers
+// per thread, so two workgroups share a CU and one's loads and stores overlap
+// the other's matrix products.
+constexpr int TKC = 64;  // K chunk
+using TrailTile = MfmaTile<128, 64, TKC, false>;
 
-__global__ __launch_bounds__(256) void trailing_kernel(float* __restrict__ Wc,
+__global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ Wc,
                                                        const float* __restrict__ Err,
                                                        const float* __restrict__ U,
                                                        int64_t d_out, int64_t d_in, int64_t b0,
                                                        int kb, int64_t n0) {
   __shared__ __attribute__((aligned(16))) float lds[TrailTile::lds_floats];
   const int64_t ncols = d_in - n0;
-  const int ntn = (int)ceil_div(ncols, 128);
+  const int ntn = (int)ceil_div(ncols, 64);
   const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
-  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * 128;
+  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * 64;
   const int rows = (int)min<int64_t>(128, d_out - m0);
-  const int cols = (int)min<int64_t>(128, d_in - n0t);
+  const int cols = (int)min<int64_t>(64, d_in - n0t);
   f32x16 acc[TrailTile::FM][TrailTile::FN];
   TrailTile::zero(acc);
-  TrailTile::load_pq(lds, Err + m0 * d_in + b0, d_in, rows, kb, U + b0 * d_in + n0t, d_in, kb,
-                     cols);
-  __syncthreads();
-  TrailTile::mma(lds, acc);
+  for (int kc = 0; kc < kb; kc += TKC) {
+    const int kn = min(TKC, kb - kc);
+    if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
+    TrailTile::load_pq(lds, Err + m0 * d_in + b0 + kc, d_in, rows, kn,
+                       U + (b0 + kc) * d_in + n0t, d_in, kn, cols);
+    __syncthreads();
+    TrailTile::mma(lds, acc);
+  }
   TrailTile::store<true>(Wc + m0 * d_in + n0t, d_in, rows, cols, acc);
 }
 
@@ -376,7 +384,7 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
     const int kb = (int)std::min<int64_t>(QB, d_in - b0);
     const int64_t n0 = b0 + kb;
     if (n0 < d_in) {
-      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - n0, 128);
+      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - n0, 64);
       hipLaunchKernelGGL(trailing_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
                          (const float*)w.Err, U, d_out, d_in, b0, kb, n0);
     }
