@@ -23,6 +23,7 @@ namespace gptq {
 namespace {
 
 constexpr int NB = 64;
+constexpr int UG = 4;   // steps per delayed trailing update
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -355,39 +356,74 @@ __global__ __launch_bounds__(256) void fac_panel_kernel(float* __restrict__ A,
   }
 }
 
-// Trailing updates of both factorizations.
+// Updates of both factorizations by the panels of steps m in [mlo, mhi)
+// (delayed, grouped updates: the trailing matrix is read and written once per
+// group of steps instead of once per step):
+//   L tiles  A_ij -= sum_m L_im L_jm^T
+//   M tiles  B_ij -= sum_m L_im M_mj   (only m >= j contributes: M is lower)
+// PART 1 (before step kc of a group, mhi = kc): block column kc of L (tiles
+//   (i, kc), i >= kc) and block row kc of B (tiles (kc, j), j < kc) -- what
+//   the diagonal and panel kernels of step kc read;
+// PART 2 (after the group, mhi = its end): L tiles (i, j) with i >= j >= mhi
+//   and B tiles (i, j) with i >= mhi, j < mhi.
+// Each step m is one K = 64 chunk through LDS, accumulated in registers.
+template <int PART>
 __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
-                                                         float* __restrict__ M, int d, int k,
-                                                         int nb, const int32_t* status) {
+                                                         float* __restrict__ M, int d, int nb,
+                                                         int mlo, int mhi,
+                                                         const int32_t* status) {
   if (*status != 0) return;
   __shared__ __attribute__((aligned(16))) float lds[TILE_LDS];
-  const int k0 = k * NB, kb = min(NB, d - k0);
-  const int T = nb - k - 1;
-  const int ta = T * (T + 1) / 2;
   const int wg = blockIdx.x;
-  if (wg < ta) {
-    int ii, jj;
-    tri_coords(wg, ii, jj);
-    const int i0 = (k + 1 + ii) * NB, j0 = (k + 1 + jj) * NB;
-    const int ib = min(NB, d - i0), jb = min(NB, d - j0);
+  bool ltile;
+  int bi, bj;  // output block coordinates
+  if (PART == 1) {
+    const int T = nb - mhi;
+    ltile = wg < T;
+    bi = ltile ? mhi + wg : mhi;
+    bj = ltile ? mhi : wg - T;
+  } else {
+    const int T = nb - mhi;
+    const int ta = T * (T + 1) / 2;
+    ltile = wg < ta;
+    if (ltile) {
+      int ii, jj;
+      tri_coords(wg, ii, jj);
+      bi = mhi + ii;
+      bj = mhi + jj;
+    } else {
+      const int idx = wg - ta;
+      bi = mhi + idx / mhi;
+      bj = idx % mhi;
+    }
+  }
+  const int i0 = bi * NB, j0 = bj * NB;
+  const int ib = min(NB, d - i0), jb = min(NB, d - j0);
+  if (ltile) {
     f32x16 acc[TileT::FM][TileT::FN];
     TileT::zero(acc);
-    TileT::load_p(lds, A + (int64_t)i0 * d + k0, d, ib, kb);  // P = L_ik
-    TileT::load_q(lds, A + (int64_t)j0 * d + k0, d, jb, kb);  // Q^T = L_jk
-    __syncthreads();
-    TileT::mma(lds, acc);
+    for (int m = mlo; m < mhi; ++m) {
+      const int m0 = m * NB, mb = min(NB, d - m0);
+      if (m > mlo) __syncthreads();
+      TileT::load_pq(lds, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
+                     A + (int64_t)j0 * d + m0, d, jb, mb);       // Q^T = L_jm
+      __syncthreads();
+      TileT::mma(lds, acc);
+    }
     tile_store<TileT, true>(A + (int64_t)i0 * d + j0, d, ib, jb, acc);
   } else {
-    const int idx = wg - ta;
-    const int ii = idx / (k + 1), j = idx % (k + 1);
-    const int i0 = (k + 1 + ii) * NB, j0 = j * NB;
-    const int ib = min(NB, d - i0), jb = min(NB, d - j0);
+    const int ms = max(mlo, bj);
+    if (ms >= mhi) return;
     f32x16 acc[TileN::FM][TileN::FN];
     TileN::zero(acc);
-    TileN::load_p(lds, A + (int64_t)i0 * d + k0, d, ib, kb);  // P = L_ik
-    TileN::load_q(lds, M + (int64_t)k0 * d + j0, d, kb, jb);  // Q = M_kj
-    __syncthreads();
-    TileN::mma(lds, acc);
+    for (int m = ms; m < mhi; ++m) {
+      const int m0 = m * NB, mb = min(NB, d - m0);
+      if (m > ms) __syncthreads();
+      TileN::load_pq(lds, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
+                     M + (int64_t)m0 * d + j0, d, mb, jb);       // Q = M_mj
+      __syncthreads();
+      TileN::mma(lds, acc);
+    }
     tile_store<TileN, true>(M + (int64_t)i0 * d + j0, d, ib, jb, acc);
   }
 }
@@ -420,19 +456,29 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
                      (const double*)w.scal, w.A, w.M);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Steps in groups of UG: before each step of a group, its block column
+  // (and block row of B) receives the group's earlier panels; after the
+  // group, everything further right receives all of the group's panels at
+  // once (K = 64 UG).
   const int nb = (int)ceil_div(d, NB);
-  for (int k = 0; k < nb; ++k) {
-    hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv, d, k,
-                       dev_status);
-    const int nrow = nb - k - 1;
-    if (nrow + k > 0)
-      hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
-                         (const float*)w.Dinv, d, k, nrow, (const int32_t*)dev_status);
-    const int T = nb - k - 1;
-    const int tiles = T * (T + 1) / 2 + T * (k + 1);
+  for (int g0 = 0; g0 < nb; g0 += UG) {
+    const int gend = std::min(nb, g0 + UG);
+    for (int k = g0; k < gend; ++k) {
+      if (k > g0)
+        hipLaunchKernelGGL(fac_update_kernel<1>, dim3(nb - k + k), dim3(256), 0, stream, w.A, w.M,
+                           d, nb, g0, k, (const int32_t*)dev_status);
+      hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv, d, k,
+                         dev_status);
+      const int nrow = nb - k - 1;
+      if (nrow + k > 0)
+        hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
+                           (const float*)w.Dinv, d, k, nrow, (const int32_t*)dev_status);
+    }
+    const int T = nb - gend;
+    const int tiles = T * (T + 1) / 2 + T * gend;
     if (tiles > 0)
-      hipLaunchKernelGGL(fac_update_kernel, dim3(tiles), dim3(256), 0, stream, w.A, w.M, d, k, nb,
-                         (const int32_t*)dev_status);
+      hipLaunchKernelGGL(fac_update_kernel<2>, dim3(tiles), dim3(256), 0, stream, w.A, w.M, d, nb,
+                         g0, gend, (const int32_t*)dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
