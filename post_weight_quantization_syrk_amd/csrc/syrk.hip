@@ -40,6 +40,41 @@ __device__ __forceinline__ void tri_coords(int t, int& ti, int& tj) {
   tj = t - i * (i + 1) / 2;
 }
 
+// Lower-triangle tile of workgroup slot t (0 <= t < ntp, ntp a multiple of
+// 8).  Slots t = 8 i + x go to XCD x; XCD x takes ranks x ntp/8 .. + ntp/8 - 1
+// of an order that walks 4 x 4 blocks of tiles (row-major over the lower
+// triangle of blocks, row-major inside a block), so consecutive ranks share
+// panels.  Returns false for ranks past the last tile.
+__device__ __forceinline__ bool tile_of_id(int t, int ntp, int ntri, int& ti, int& tj) {
+  constexpr int SBK = 4;
+  const int r = (t & 7) * (ntp >> 3) + (t >> 3);
+  if (r >= ntri) return false;
+  const int ntile = (int)((sqrtf(8.0f * (float)ntri + 1.0f) - 1.0f) * 0.5f + 0.5f);
+  const int nblk = (ntile + SBK - 1) / SBK;
+  int rr = r;
+  for (int bi = 0; bi < nblk; ++bi) {
+    const int h = min(SBK, ntile - bi * SBK);
+    for (int bj = 0; bj <= bi; ++bj) {
+      const int w = min(SBK, ntile - bj * SBK);
+      const int sz = (bi == bj) ? h * (h + 1) / 2 : h * w;
+      if (rr < sz) {
+        if (bi != bj) {
+          ti = bi * SBK + rr / w;
+          tj = bj * SBK + rr % w;
+        } else {
+          int k = 0;
+          while ((k + 1) * (k + 2) / 2 <= rr) ++k;
+          ti = bi * SBK + k;
+          tj = bj * SBK + rr - k * (k + 1) / 2;
+        }
+        return true;
+      }
+      rr -= sz;
+    }
+  }
+  return false;
+}
+
 struct SyrkArgs {
   const uint16_t* X;
   int64_t ldx;
@@ -259,13 +294,16 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   const uint32_t lds_off = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)lds;
 
   // Split-major order: the workgroups resident at any time (about one per
-  // CU) cover all tiles of one or two token ranges, so every XCD streams the
-  // same X rows at about the same time and its L2 misses for them are
-  // served by the shared last-level cache rather than by HBM, once each.
-  const int tile = blockIdx.x % a.ntri;
-  const int split = blockIdx.x / a.ntri;
+  // CU) cover all tiles of one or two token ranges, so the XCDs stream the
+  // same X rows at about the same time.  Within a range, workgroup ids are
+  // handed to the 8 XCDs round-robin; tile_of_id gives each XCD a compact
+  // block of tiles, so its L2 serves one fetch of a panel's rows to several
+  // of its tiles.  Ids past the last tile (padding to a multiple of 8) exit.
+  const int ntp = (a.ntri + 7) & ~7;
+  const int split = blockIdx.x / ntp;
   int ti, tj;
-  tri_coords(tile, ti, tj);
+  if (!tile_of_id(blockIdx.x % ntp, ntp, a.ntri, ti, tj)) return;
+  const int tile = ti * (ti + 1) / 2 + tj;
   const bool diag = (ti == tj);
   const int ci = ti * TB, cj = tj * TB;
   const bool full_tile = a.vec && (ci + TB <= a.d) && (cj + TB <= a.d);
@@ -475,7 +513,7 @@ static int pick_splits(int64_t n, int ntri, int stage, double partial_cost) {
   int best = 1;
   double best_cost = 0.0;
   for (int s = 1; s <= max_s; ++s) {
-    const double rounds = (double)ceil_div((int64_t)ntri * s, 256);
+    const double rounds = (double)ceil_div((int64_t)((ntri + 7) & ~7) * s, 256);
     const double stages = (double)ceil_div(ceil_div(n, (int64_t)s), (int64_t)stage);
     const double cost = rounds * stages + partial_cost * s * ntri;
     if (s == 1 || cost < best_cost) {
@@ -512,7 +550,8 @@ hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t 
     const int vec = ((uintptr_t)X % 16 == 0) && (ldx % 8 == 0) &&
                     (2 * ldx + d) * 2 < ((int64_t)1 << 31);
     SyrkArgs a{(const uint16_t*)X, ldx, n, (int)d, plan.ntri, plan.splits, vec, plan.kper, partial};
-    hipLaunchKernelGGL(syrk_bf16_kernel, dim3(grid), dim3(NTHR), 0, stream, a);
+    const int ntp = (plan.ntri + 7) & ~7;
+    hipLaunchKernelGGL(syrk_bf16_kernel, dim3(ntp * plan.splits), dim3(NTHR), 0, stream, a);
     hipLaunchKernelGGL(splitk_reduce_kernel<TB>, dim3(plan.ntri * (TB * TB / 4 / 1024)), dim3(256),
                        0, stream, H, (int)d, partial, plan.ntri, plan.splits);
   } else {
