@@ -114,17 +114,23 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
 
 // Diagonal block: L_kk = chol(A_kk) and Dinv = L_kk^{-1}, by 256 threads in
 // four 16-column sub-steps S = [s0, s0 + 16), s0 = 16 s:
-//   A: wave 0 factors the 16 x 16 block A_SS in registers (lane r of each
-//      16-lane row holds row r; pivots and column values are broadcast with
-//      DPP row broadcasts, so the 16 dependent pivot steps need no barrier and
-//      no scalar registers) and inverts it (M_SS);
-//      meanwhile waves 1-3 form R = L_{S,0:s0} M_{0:s0,0:s0}, which the rows
+//   A: wave 0 factors the 16 x 16 block A_SS in registers and inverts it.
+//      Lane (g, r) (16-lane row g, lane r of the row) holds row r of the
+//      symmetric Schur complement and columns 4g .. 4g+3 of row r of the
+//      inverse; pivot and column values are broadcast with DPP row
+//      broadcasts, so the 16 dependent pivot steps need no barrier and no
+//      scalar registers.  The four row groups repeat the factorization and
+//      share the inverse.
+//      Meanwhile waves 1-3 form R = L_{S,0:s0} M_{0:s0,0:s0}, which the rows
 //      of L^{-1} below need;
 //   B: the panel L_{i,S} = A_{i,S} M_SS^T for rows i below S, and the row
 //      block M_{S,0:s0} = -M_SS R of L^{-1};
 //   C: the rank-16 update A_{i,j} -= L_{i,S} L_{j,S}^T of the rows below S.
-// A failed pivot (not positive or not finite) is replaced by 1 so the
-// factorization finishes with finite values; the first one is reported.
+// The upper triangles of the LDS copies of L and L^{-1} hold zeros, so the
+// triangular products run over full index ranges without per-lane branches.
+// A pivot that is not positive and finite turns its diagonal entry of L into
+// NaN or 0 and every later pivot into NaN; the first diagonal entry of L that
+// is not positive and finite is the first failed pivot, and is reported.
 constexpr int SB = 16;
 constexpr int PP16 = 20;  // LDS pitch (floats) of the 16-wide panel copy: 16-byte rows
 
@@ -137,7 +143,6 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
   __shared__ float mtile[NB][NB + 1];  // L_kk^{-1} (lower)
   __shared__ float rbuf[SB][NB + 1];   // R of the current sub-step
   __shared__ __attribute__((aligned(16))) float pan[NB][PP16];  // panel copy L_{i,S}
-  __shared__ int bad_s;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int k0 = k * NB;
@@ -158,7 +163,15 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
       mtile[rr][cc] = 0.0f;
     }
   }
-  if (t == 0) bad_s = 0;
+  // Per-lane masks of the in-register factorization (row r = lane % 16):
+  // ngt[c] = -1 below pivot c, else 0; eqf[c] = 1 on the pivot row.
+  const int r = lane & (SB - 1), grp = lane >> 4;
+  float ngt[SB], eqf[SB];
+#pragma unroll
+  for (int c = 0; c < SB; ++c) {
+    ngt[c] = (r > c) ? -1.0f : 0.0f;
+    eqf[c] = (r == c) ? 1.0f : 0.0f;
+  }
   __syncthreads();
 
   StaticFor<0, NB / SB>::run([&](auto Sv) {
@@ -166,52 +179,50 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
     constexpr int rows = NB - s0 - SB;  // rows below the sub-block
     // ---------------- A
     if (wave == 0) {
-      const int r = lane & (SB - 1);  // lanes 16..63 repeat rows 0..15; only 0..15 write
-      float a[SB], m[SB];
+      // a[j]: row r of the symmetric Schur complement of A_SS (both halves,
+      // so no lane ever holds values that are not bounded by the matrix's).
+      // mv[q]: row r of the partially eliminated identity, columns 4 grp + q;
+      // row c of L_SS^{-1} is mv of lane c times 1 / L_cc.
+      float a[SB], mv[4];
 #pragma unroll
-      for (int j = 0; j < SB; ++j) {
-        a[j] = (j <= r) ? tile[s0 + r][s0 + j] : 0.0f;
-        m[j] = (j == r) ? 1.0f : 0.0f;
-      }
-      int bad = 0;
+      for (int j = 0; j < SB; ++j)
+        a[j] = (j <= r) ? tile[s0 + r][s0 + j] : tile[s0 + j][s0 + r];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mv[q] = eqf[4 * grp + q];
+      float myinv = 0.0f;
       StaticFor<0, SB>::run([&](auto Cv) {
         constexpr int c = decltype(Cv)::value;
-        float piv = row_bcast<c>(a[c]);
-        const bool ok = (piv > 0.0f) && (piv < 3.0e38f);
-        bad = (bad == 0 && !ok) ? (s0 + c + 1) : bad;
-        piv = ok ? piv : 1.0f;
-        const float inv = __builtin_amdgcn_rsqf(piv);  // 1/sqrt, within 1 ulp
-        const float l = (r > c) ? a[c] * inv : 0.0f;   // L[r][c] below the diagonal
-        a[c] = (r > c) ? l : ((r == c) ? piv * inv : 0.0f);
+        const float inv = __builtin_amdgcn_rsqf(row_bcast<c>(a[c]));  // 1/sqrt, within 1 ulp
+        const float l = a[c] * inv;  // L[r][c] below the pivot, L[c][c] on it
+        a[c] = l;
+        const float nl = l * ngt[c];  // -L[r][c] below the pivot, 0 elsewhere
         StaticFor<c + 1, SB>::run([&](auto Jv) {
           constexpr int j = decltype(Jv)::value;
-          a[j] = fmaf(-l, row_bcast<j>(l), a[j]);      // only the lower part is used
+          a[j] = fmaf(row_bcast<j>(l), nl, a[j]);
         });
-        const float sc = (r == c) ? inv : 1.0f;        // completes row c of L^{-1}
-        StaticFor<0, c + 1>::run([&](auto Qv) {
-          constexpr int q = decltype(Qv)::value;
-          m[q] *= sc;
-          m[q] = fmaf(-l, row_bcast<c>(m[q]), m[q]);   // eliminate below (l = 0 above)
-        });
-      });
-      if (lane < SB) {
+        const float nlm = nl * inv;  // -L[r][c] / L[c][c]
 #pragma unroll
-        for (int j = 0; j < SB; ++j) {
-          tile[s0 + r][s0 + j] = (j <= r) ? a[j] : 0.0f;
-          mtile[s0 + r][s0 + j] = (j <= r) ? m[j] : 0.0f;
-        }
+        for (int q = 0; q < 4; ++q) mv[q] = fmaf(row_bcast<c>(mv[q]), nlm, mv[q]);
+        myinv = fmaf(inv, eqf[c], myinv);
+      });
+      if (grp == 0) {
+#pragma unroll
+        for (int j = 0; j < SB; ++j) tile[s0 + r][s0 + j] = (j <= r) ? a[j] : 0.0f;
       }
-      if (lane == 0 && bad != 0) bad_s = (bad_s == 0 || bad < bad_s) ? bad : bad_s;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mtile[s0 + r][s0 + 4 * grp + q] = mv[q] * myinv;
     } else if constexpr (s > 0) {
-      // R[r][c] = sum_{m=c}^{s0-1} L[s0+r][m] M[m][c]: thread (c, 4 rows)
+      // R[r][c] = sum_{m<s0} L[s0+r][m] M[m][c] (M[m][c] = 0 for m < c):
+      // thread (c, 4 rows)
       const int e = t - 64;
       if (e < 4 * s0) {
         const int c = e % s0, r0 = 4 * (e / s0);
         float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int mm = c; mm < s0; ++mm) {
-          const float mv = mtile[mm][c];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = fmaf(tile[s0 + r0 + i][mm], mv, acc[i]);
+        for (int mm = 0; mm < s0; ++mm) {
+          const float mvv = mtile[mm][c];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = fmaf(tile[s0 + r0 + i][mm], mvv, acc[i]);
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) rbuf[r0 + i][c] = acc[i];
@@ -220,9 +231,9 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
     __syncthreads();
     // ---------------- B
     // Threads [0, 4 rows): panel row i, columns 4jg..4jg+3:
-    //   L[i][s0+j] = sum_{q<=j} A[i][s0+q] M_SS[j][q].
+    //   L[i][s0+j] = sum_q A[i][s0+q] M_SS[j][q]   (M_SS[j][q] = 0 for q > j).
     // Threads [4 rows, 4 rows + 4 s0): row block of L^{-1}, column c, rows
-    //   4g..4g+3:  M[s0+r][c] = -sum_{p<=r} M_SS[r][p] R[p][c].
+    //   4g..4g+3:  M[s0+r][c] = -sum_p M_SS[r][p] R[p][c]   (M_SS[r][p] = 0 for p > r).
     float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     if (t < 4 * rows) {
       const int i = s0 + SB + (t >> 2), j0 = 4 * (t & 3);
@@ -230,8 +241,7 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
       for (int q = 0; q < SB; ++q) {
         const float av = tile[i][s0 + q];
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (q <= j0 + u) pv[u] = fmaf(av, mtile[s0 + j0 + u][s0 + q], pv[u]);
+        for (int u = 0; u < 4; ++u) pv[u] = fmaf(av, mtile[s0 + j0 + u][s0 + q], pv[u]);
       }
     }
     if constexpr (s > 0) {
@@ -243,8 +253,7 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
         for (int p = 0; p < SB; ++p) {
           const float rv = rbuf[p][c];
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            if (p <= g0 + u) acc[u] = fmaf(mtile[s0 + g0 + u][s0 + p], rv, acc[u]);
+          for (int u = 0; u < 4; ++u) acc[u] = fmaf(mtile[s0 + g0 + u][s0 + p], rv, acc[u]);
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) mtile[s0 + g0 + u][c] = -acc[u];
@@ -282,11 +291,19 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
       __syncthreads();
     }
   });
-  if (bad_s != 0) {
-    if (t == 0) *status = d - (k0 + bad_s - 1);
-    return;
+  {
+    // First failed pivot: the first diagonal entry of L that is not positive
+    // and finite (every wave takes the same decision).
+    const float dg = tile[lane][lane];
+    const uint64_t badm = __ballot(!(dg > 0.0f && dg < INFINITY));
+    if (badm != 0) {
+      if (t == 0) *status = d - (k0 + __ffsll((unsigned long long)badm) - 1);
+      return;
+    }
   }
-  // Global stores, row-contiguous (16 threads per 64-float row).
+  // Global stores, row-contiguous (16 threads per 64-float row).  The upper
+  // triangles of both LDS copies are zero, so whole rows are written.
+  const bool vec = (kb == NB) && (d % 4 == 0);
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
     const int rr = 16 * u + (t >> 4), c0 = 4 * (t & 15);
@@ -294,18 +311,21 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       lv[e] = tile[rr][c0 + e];
-      mv[e] = (c0 + e <= rr) ? mtile[rr][c0 + e] : 0.0f;
+      mv[e] = mtile[rr][c0 + e];
     }
     *(float4*)(Dinv + rr * NB + c0) = make_float4(mv[0], mv[1], mv[2], mv[3]);
-    if (rr < kb) {
-      float* arow = A + (int64_t)(k0 + rr) * d + k0;
-      float* mrow_g = M + (int64_t)(k0 + rr) * d + k0;
+    float* arow = A + (int64_t)(k0 + rr) * d + k0;
+    float* mrow_g = M + (int64_t)(k0 + rr) * d + k0;
+    if (vec) {
+      *(float4*)(arow + c0) = make_float4(lv[0], lv[1], lv[2], lv[3]);
+      *(float4*)(mrow_g + c0) = make_float4(mv[0], mv[1], mv[2], mv[3]);
+    } else if (rr < kb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = c0 + e;
         if (c < kb) {
-          if (c <= rr) arow[c] = lv[e];
-          mrow_g[c] = mv[e];  // zero above the diagonal
+          arow[c] = lv[e];
+          mrow_g[c] = mv[e];
         }
       }
     }

@@ -129,7 +129,7 @@ def _spd(d, seed, n=None):
     return (2.0 * x.T @ x).astype(np.float32)
 
 
-@pytest.mark.parametrize("d", [1, 5, 64, 100, 256, 1000])
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 130, 256, 1000])
 def test_prepare_matches_oracle(d):
     H32 = _spd(d, d)
     H = dev_f32(np.tril(H32))
