@@ -19,6 +19,7 @@
 #include "mfma_f32.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <cmath>
 #include <cstdlib>
 
@@ -283,6 +284,31 @@ __device__ __forceinline__ void wait_vm(int n) {
     __asm__ volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// LDS transpose read at an LDS byte address (the constant part of the
+// address folds into the instruction's offset field).
+__device__ __forceinline__ s16x4 lds_tr_at(uint32_t off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)off);
+}
+__device__ __forceinline__ bf16x8 afrag_at(uint32_t off) {
+  s16x4 lo = lds_tr_at(off);
+  s16x4 hi = lds_tr_at(off + 4 * AROW);
+  typedef __attribute__((ext_vector_type(8))) short s16x8;
+  s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, v);
+}
+// Direct load with M0 = lds_base + IMM (IMM a compile-time constant).
+template <uint32_t IMM>
+__device__ __forceinline__ void dma16_imm(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  __asm__ volatile("s_add_u32 m0, %2, %3\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :
+                   : "v"(voff), "s"(sbase), "s"(lds_base), "i"(IMM)
+                   : "memory", "m0");
+}
+template <int N>
+__device__ __forceinline__ void wait_vm_n() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Fragments of one stage (two 16-token MFMA steps) for one wave.
 struct StageFrags {
   bf16x8 a[ABK / 16][4];
@@ -419,6 +445,94 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
     read_stage(0, f0);
   }
   int s = 0;
+  // Steady state of a full tile: every stage in flight is a full direct-load
+  // stage.  Six steps per iteration, so the LDS slot (s % 3) and the fragment
+  // set (s % 2) are compile-time constants; load addresses advance by one
+  // scalar add per step, and LDS read and load destination offsets are
+  // immediates on precomputed per-lane bases.
+  const int nfull = full_tile ? (int)((ke - kb) / ABK) : 0;
+  const bool fast = full_tile && (int64_t)(ABK * a.ldx + a.d) * 2 < ((int64_t)1 << 31);
+  auto fast_loop = [&](auto DiagC) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(DiagC)::value;
+    constexpr uint32_t OPB = DIAG ? 0u : (uint32_t)AOP;
+    // per-lane LDS read bases of slot 1 (stage 1 is read during step 0);
+    // moved to the next slot after every step
+    uint32_t rdA[4], rdB[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      rdA[i] = lds_off + ASTAGE + aoff(frow, 128 * wm + 32 * i + fcol);
+      rdB[i] = lds_off + ASTAGE + OPB + aoff(frow, 128 * wn + 32 * i + fcol);
+    }
+    const uint32_t rowoff = __builtin_amdgcn_readfirstlane((uint32_t)(RPW * wave * a.ldx * 2));
+    const uint32_t rowstep = (uint32_t)(4 * a.ldx);  // two rows, bytes
+    const uint32_t ldsw = __builtin_amdgcn_readfirstlane(lds_off + RPW * wave * AROW);
+    const uint16_t* xs = a.X + (kb + (int64_t)ANS * ABK) * a.ldx;  // stage s + 3
+    const int64_t xstep = (int64_t)ABK * a.ldx;
+    for (; s + 6 + ANS <= nfull; s += 6) {
+      StaticFor<0, 6>::run([&](auto St) __attribute__((always_inline)) {
+        constexpr int st = decltype(St)::value;
+        constexpr int SLOT = st % ANS, NSLOT = (st + 1) % ANS;
+        static_assert(ANS == 3, "slot rotation");
+        StageFrags& cur = (st % 2 == 0) ? f0 : f1;
+        StageFrags& nxt = (st % 2 == 0) ? f1 : f0;
+        wait_vm_n<DIAG ? NQ : 2 * NQ>();
+        __syncthreads();
+        const uint64_t xb = (uint64_t)(uintptr_t)xs;
+        const uint32_t blo = __builtin_amdgcn_readfirstlane((uint32_t)xb);
+        const uint32_t bhi = __builtin_amdgcn_readfirstlane((uint32_t)(xb >> 32));
+        const void* sb = (const void*)(uintptr_t)(((uint64_t)bhi << 32) | blo);
+        StaticFor<0, 2 * (ABK / 16)>::run([&](auto G) __attribute__((always_inline)) {
+          constexpr int g = decltype(G)::value;
+          constexpr int kk = g >> 1;
+          // row-pair offset of this load, kept inside the loop (hoisting the
+          // twelve per-lane offsets out of it would spill them)
+          uint32_t ro = rowoff + (uint32_t)g * rowstep;
+          __asm__ volatile("" : "+s"(ro));
+          dma16_imm<(uint32_t)(SLOT * ASTAGE + 2 * g * AROW)>(sb, offA.v[g & 1] + ro, ldsw);
+          if constexpr (!DIAG)
+            dma16_imm<(uint32_t)(SLOT * ASTAGE + AOP + 2 * g * AROW)>(sb, offB.v[g & 1] + ro,
+                                                                       ldsw);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if constexpr ((g & 1) == 0)
+              nxt.a[kk][i] = afrag_at(rdA[i] + kk * 16 * AROW);
+            else
+              nxt.b[kk][i] = afrag_at(rdB[i] + kk * 16 * AROW);
+          }
+#pragma unroll
+          for (int mi = 2 * (g & 1); mi < 2 * (g & 1) + 2; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < 4; ++ni)
+              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][mi], cur.b[kk][ni],
+                                                                   acc[mi][ni], 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        xs += xstep;
+        // next step reads slot (st + 2) % 3
+        constexpr int DS = (NSLOT == ANS - 1) ? -(ANS - 1) * ASTAGE : ASTAGE;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          rdA[i] += (uint32_t)DS;
+          rdB[i] += (uint32_t)DS;
+          // opaque to the compiler: folding the slot rotation into the read
+          // offsets would exceed the 16-bit offset field
+          __asm__ volatile("" : "+v"(rdA[i]), "+v"(rdB[i]));
+        }
+      });
+    }
+  };
+  if (fast && nst > 0) {
+    if (diag)
+      fast_loop(std::true_type{});
+    else
+      fast_loop(std::false_type{});
+  }
   for (; s + 1 < nst; s += 2) {
     step(s, f0, f1);
     step(s + 1, f1, f0);
