@@ -182,6 +182,23 @@ struct MfmaTile {
     }
   }
 
+  // Set every accumulator element to f(row, col) of its place in the tile.
+  template <class F>
+  __device__ static void set_each(f32x16 (&acc)[FM][FN], F&& f) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * WM + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = wn * WN + 32 * b + (lane & 31);
+          acc[a][b][r] = f(row, col);
+        }
+  }
+
   // Visit every accumulator element with its (row, col) inside the tile.
   template <class F>
   __device__ static void for_each(const f32x16 (&acc)[FM][FN], F&& f) {

@@ -288,11 +288,14 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]   (fp32 MFMA, 128 x 64 tiles).
-// K = 128 runs as two chunks of 64 through 57 KiB of LDS and <= 256 registers
-// per thread, so two workgroups share a CU and one's loads and stores overlap
-// the other's matrix products.
-constexpr int TKC = 64;  // K chunk
+// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]  (fp32 MFMA, 128 x 64 tiles).
+// The tile of Wc is loaded into the accumulators first and the error operand
+// is negated on its way into LDS, so the products accumulate onto Wc and the
+// final store needs no read.  K runs in chunks of 32 through 46 KiB of LDS,
+// the next chunk's loads in flight while the current one multiplies; two
+// workgroups share a CU, one's loads and stores overlapping the other's
+// matrix products.
+constexpr int TKC = 32;  // K chunk
 using TrailTile = MfmaTile<128, 64, TKC, false>;
 
 __global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ Wc,
@@ -300,24 +303,62 @@ __global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ Wc
                                                        const float* __restrict__ U,
                                                        int64_t d_out, int64_t d_in, int64_t b0,
                                                        int kb, int64_t n0) {
+  constexpr int TM = 128, TN = 64;
+  constexpr int NP = TM * TKC / 256, NQ = TKC * TN / 256;
   __shared__ __attribute__((aligned(16))) float lds[TrailTile::lds_floats];
   const int64_t ncols = d_in - n0;
-  const int ntn = (int)ceil_div(ncols, 64);
-  const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 128;
-  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * 64;
-  const int rows = (int)min<int64_t>(128, d_out - m0);
-  const int cols = (int)min<int64_t>(64, d_in - n0t);
+  const int ntn = (int)ceil_div(ncols, TN);
+  const int64_t m0 = (int64_t)(blockIdx.x / ntn) * TM;
+  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * TN;
+  const int rows = (int)min<int64_t>(TM, d_out - m0);
+  const int cols = (int)min<int64_t>(TN, d_in - n0t);
   f32x16 acc[TrailTile::FM][TrailTile::FN];
-  TrailTile::zero(acc);
-  for (int kc = 0; kc < kb; kc += TKC) {
+  float* C = Wc + m0 * d_in + n0t;
+  // the tile of Wc into the accumulators (clamped addresses; masked at the store)
+  TrailTile::set_each(acc, [&](int row, int col) {
+    return C[(int64_t)(row < rows ? row : rows - 1) * d_in + (col < cols ? col : cols - 1)];
+  });
+  const float* P = Err + m0 * d_in + b0;
+  const float* Q = U + b0 * d_in + n0t;
+  float vp[NP], vq[NQ];
+  auto gload = [&](int kc) __attribute__((always_inline)) {
     const int kn = min(TKC, kb - kc);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / TKC, c = e % TKC;
+      vp[u] = P[(int64_t)(r < rows ? r : rows - 1) * d_in + kc + (c < kn ? c : kn - 1)];
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / TN, c = e % TN;
+      vq[u] = Q[(int64_t)(kc + (r < kn ? r : kn - 1)) * d_in + (c < cols ? c : cols - 1)];
+    }
+  };
+  auto lstore = [&](int kc) __attribute__((always_inline)) {
+    const int kn = min(TKC, kb - kc);
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / TKC, c = e % TKC;
+      lds[r * TrailTile::PP + c] = (r < rows && c < kn) ? -vp[u] : 0.0f;
+    }
+    float* lq = lds + TM * TrailTile::PP;
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / TN, c = e % TN;
+      lq[r * TrailTile::QPITCH + c] = (r < kn && c < cols) ? vq[u] : 0.0f;
+    }
+  };
+  gload(0);
+  for (int kc = 0; kc < kb; kc += TKC) {
     if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
-    TrailTile::load_pq(lds, Err + m0 * d_in + b0 + kc, d_in, rows, kn,
-                       U + (b0 + kc) * d_in + n0t, d_in, kn, cols);
+    lstore(kc);
     __syncthreads();
+    if (kc + TKC < kb) gload(kc + TKC);
     TrailTile::mma(lds, acc);
   }
-  TrailTile::store<true>(Wc + m0 * d_in + n0t, d_in, rows, cols, acc);
+  TrailTile::for_each(acc, [&](int row, int col, float v) {
+    if (row < rows && col < cols) C[(int64_t)row * d_in + col] = v;
+  });
 }
 
 // ---- pack -------------------------------------------------------------------
