@@ -134,35 +134,54 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
 constexpr int SB = 16;
 constexpr int PP16 = 20;  // LDS pitch (floats) of the 16-wide panel copy: 16-byte rows
 
-__global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
-                                                       float* __restrict__ M,
-                                                       float* __restrict__ Dinv, int d, int k,
-                                                       int32_t* status) {
-  if (*status != 0) return;
-  __shared__ float tile[NB][NB + 1];   // A_kk, becomes L_kk (lower)
-  __shared__ float mtile[NB][NB + 1];  // L_kk^{-1} (lower)
-  __shared__ float rbuf[SB][NB + 1];   // R of the current sub-step
-  __shared__ __attribute__((aligned(16))) float pan[NB][PP16];  // panel copy L_{i,S}
+struct DiagLds {
+  float tile[NB][NB + 1];   // A_kk, becomes L_kk (lower)
+  float mtile[NB][NB + 1];  // L_kk^{-1} (lower)
+  float rbuf[SB][NB + 1];   // R of the current sub-step
+  alignas(16) float pan[NB][PP16];  // panel copy L_{i,S}
+};
+constexpr size_t DIAG_LDS_FLOATS = (sizeof(DiagLds) + 3) / 4;
+
+// LDS copy of the diagonal block entry (rr, cc) from its value v: lower
+// triangle, identity past the matrix edge (kb = valid rows/columns).
+__device__ __forceinline__ float diag_entry(int rr, int cc, int kb, float v) {
+  return (rr < kb && cc < kb) ? ((cc <= rr) ? v : 0.0f) : (rr == cc ? 1.0f : 0.0f);
+}
+
+// A_kk from global memory into the LDS copies (batched, unconditional loads
+// from clamped addresses, masked afterwards); L^{-1} starts at zero.
+__device__ __forceinline__ void diag_load(DiagLds& L, const float* __restrict__ A, int d, int k) {
+  const int t = threadIdx.x;
+  const int k0 = k * NB;
+  const int kb = min(NB, d - k0);
+  float v[16];
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = u * 256 + t, rr = e >> 6, cc = e & 63;
+    const int r2 = rr < kb ? rr : kb - 1, c2 = cc < kb ? cc : kb - 1;
+    v[u] = A[(int64_t)(k0 + r2) * d + k0 + c2];
+  }
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int e = u * 256 + t, rr = e >> 6, cc = e & 63;
+    L.tile[rr][cc] = diag_entry(rr, cc, kb, v[u]);
+    L.mtile[rr][cc] = 0.0f;
+  }
+}
+
+// The factorization proper, from the LDS copies (filled and published by a
+// barrier); writes L_kk and L_kk^{-1} to A and M and L_kk^{-1} to Dinv.
+__device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
+                                            float* __restrict__ M, float* __restrict__ Dinv,
+                                            int d, int k, int32_t* status) {
+  auto& tile = L.tile;
+  auto& mtile = L.mtile;
+  auto& rbuf = L.rbuf;
+  auto& pan = L.pan;
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int k0 = k * NB;
   const int kb = min(NB, d - k0);
-  {
-    // batched, unconditional loads (clamped addresses), masked afterwards
-    float v[16];
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + t, rr = e >> 6, cc = e & 63;
-      const int r2 = rr < kb ? rr : kb - 1, c2 = cc < kb ? cc : kb - 1;
-      v[u] = A[(int64_t)(k0 + r2) * d + k0 + c2];
-    }
-#pragma unroll
-    for (int u = 0; u < 16; ++u) {
-      const int e = u * 256 + t, rr = e >> 6, cc = e & 63;
-      tile[rr][cc] = (rr < kb && cc < kb) ? ((cc <= rr) ? v[u] : 0.0f) : (rr == cc ? 1.0f : 0.0f);
-      mtile[rr][cc] = 0.0f;
-    }
-  }
   // Per-lane masks of the in-register factorization (row r = lane % 16):
   // ngt[c] = -1 below pivot c, else 0; eqf[c] = 1 on the pivot row.
   const int r = lane & (SB - 1), grp = lane >> 4;
@@ -172,7 +191,6 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
     ngt[c] = (r > c) ? -1.0f : 0.0f;
     eqf[c] = (r == c) ? 1.0f : 0.0f;
   }
-  __syncthreads();
 
   StaticFor<0, NB / SB>::run([&](auto Sv) {
     constexpr int s = decltype(Sv)::value, s0 = SB * s;
@@ -332,6 +350,17 @@ __global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
   }
 }
 
+__global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
+                                                       float* __restrict__ M,
+                                                       float* __restrict__ Dinv, int d, int k,
+                                                       int32_t* status) {
+  if (*status != 0) return;
+  __shared__ DiagLds L;
+  diag_load(L, A, d, k);
+  __syncthreads();
+  diag_factor(L, A, M, Dinv, d, k, status);
+}
+
 using TileT = MfmaTile<NB, NB, NB, true>;   // C = P Q with Q given transposed
 using TileN = MfmaTile<NB, NB, NB, false>;  // C = P Q with Q row-major
 constexpr size_t TILE_LDS = (TileT::lds_floats > TileN::lds_floats ? TileT::lds_floats
@@ -387,13 +416,22 @@ __global__ __launch_bounds__(256) void fac_panel_kernel(float* __restrict__ A,
 // PART 2 (after the group, mhi = its end): L tiles (i, j) with i >= j >= mhi
 //   and B tiles (i, j) with i >= mhi, j < mhi.
 // Each step m is one K = 64 chunk through LDS, accumulated in registers.
+// With fuse_diag, workgroup 0 -- the one that updates the next diagonal
+// block (block mhi: tile (mhi, mhi) comes first in both parts) -- goes on to
+// factorize it: the updated block goes from its accumulators straight into the
+// factorization's LDS copies, and the factorization runs while the other
+// workgroups finish their tiles, instead of as a kernel of its own after them.
+// (It touches only block (mhi, mhi) of A and M and Dinv, which no other tile
+// of this launch reads.)
 template <int PART>
 __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
-                                                         float* __restrict__ M, int d, int nb,
-                                                         int mlo, int mhi,
-                                                         const int32_t* status) {
+                                                         float* __restrict__ M,
+                                                         float* __restrict__ Dinv, int d, int nb,
+                                                         int mlo, int mhi, int fuse_diag,
+                                                         int32_t* status) {
   if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[TILE_LDS];
+  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
   const int wg = blockIdx.x;
   bool ltile;
   int bi, bj;  // output block coordinates
@@ -429,6 +467,28 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
                      A + (int64_t)j0 * d + m0, d, jb, mb);       // Q^T = L_jm
       __syncthreads();
       TileT::mma(lds, acc);
+    }
+    if (fuse_diag && wg == 0) {
+      DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
+      float old[16];  // A_kk before this update (this workgroup's one 32 x 32 MFMA tile)
+      {
+        int n = 0;
+        TileT::for_each(acc, [&](int row, int col, float) {
+          const int r2 = row < ib ? row : ib - 1, c2 = col < ib ? col : ib - 1;
+          old[n++] = A[(int64_t)(i0 + r2) * d + j0 + c2];
+        });
+      }
+      __syncthreads();  // every wave is done with the product's LDS operands
+      {
+        int n = 0;
+        TileT::for_each(acc, [&](int row, int col, float v) {
+          L.tile[row][col] = diag_entry(row, col, ib, old[n++] - v);
+        });
+      }
+      for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
+      __syncthreads();
+      diag_factor(L, A, M, Dinv, d, bi, status);
+      return;
     }
     tile_store<TileT, true>(A + (int64_t)i0 * d + j0, d, ib, jb, acc);
   } else {
@@ -484,11 +544,15 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
   for (int g0 = 0; g0 < nb; g0 += UG) {
     const int gend = std::min(nb, g0 + UG);
     for (int k = g0; k < gend; ++k) {
+      // the diagonal block of step k is factorized by the update launch that
+      // brings it up to date (this group's part 1, or the previous group's
+      // part 2); only step 0 needs a launch of its own
       if (k > g0)
         hipLaunchKernelGGL(fac_update_kernel<1>, dim3(nb - k + k), dim3(256), 0, stream, w.A, w.M,
-                           d, nb, g0, k, (const int32_t*)dev_status);
-      hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv, d, k,
-                         dev_status);
+                           w.Dinv, d, nb, g0, k, 1, dev_status);
+      else if (k == 0)
+        hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv, d, k,
+                           dev_status);
       const int nrow = nb - k - 1;
       if (nrow + k > 0)
         hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
@@ -497,8 +561,8 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
     const int T = nb - gend;
     const int tiles = T * (T + 1) / 2 + T * gend;
     if (tiles > 0)
-      hipLaunchKernelGGL(fac_update_kernel<2>, dim3(tiles), dim3(256), 0, stream, w.A, w.M, d, nb,
-                         g0, gend, (const int32_t*)dev_status);
+      hipLaunchKernelGGL(fac_update_kernel<2>, dim3(tiles), dim3(256), 0, stream, w.A, w.M,
+                         w.Dinv, d, nb, g0, gend, 1, dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
