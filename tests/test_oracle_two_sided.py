@@ -67,7 +67,9 @@ def test_rejects_singular_basis():
 @pytest.mark.slow
 def test_cost_exponents():
     """Cubic vs quartic growth (方法: O(n^4) -> O(n^3)); fitted on small n."""
-    def t(fn, n, reps=1):
+    # best of three: the first call at each size also pays one-time costs
+    # (first touch of its intermediates) that can exceed the work itself
+    def t(fn, n, reps=3):
         Y, RL, RR = synth.two_sided_inputs(n)
         best = 1e9
         for _ in range(reps):
