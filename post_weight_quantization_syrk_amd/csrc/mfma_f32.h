@@ -9,9 +9,10 @@
 // C: register r of lane l is C[8(r/4) + 4(l/32) + r%4][l%32].
 //
 // LDS layouts (fp32 words; 64 banks of 4 bytes):
-//   P is kept row-major [m][k] with a row pitch == 2 (mod 64): the 32 lanes of
-//   an A read hit 32 rows at one column -> even banks, and the other 32 lanes
-//   (column k+1) -> odd banks.  No conflicts.  Q given transposed (Q^T
+//   P is kept row-major [m][k] with a row pitch p == 2 (mod 32): the 32 lanes
+//   of an A read hit rows r = 0..31 at one column, banks (p r) mod 64 =
+//   2 ((p/2) r mod 32) with p/2 odd -> 32 distinct even banks, and the other
+//   32 lanes (column k+1) -> odd banks.  No conflicts.  Q given transposed (Q^T
 //   row-major [n][k]) uses the same layout; Q given row-major [k][n] uses a row
 //   pitch == 32 (mod 64) so the two half-waves (rows k and k+1) fall in
 //   disjoint bank halves.
@@ -25,7 +26,7 @@ namespace gptq {
 
 template <int TM, int TN, int K, bool QT>
 struct MfmaTile {
-  static constexpr int PP = K + 2 + ((K % 64) ? 64 - (K % 64) : 0);  // == 2 (mod 64)
+  static constexpr int PP = K + 2 + ((K % 32) ? 32 - (K % 32) : 0);  // == 2 (mod 32)
   static constexpr int PQN = TN + 32 + ((TN % 64) ? 64 - (TN % 64) : 0);  // == 32 (mod 64)
   static constexpr int QROWS = QT ? TN : K;
   static constexpr int QPITCH = QT ? PP : PQN;

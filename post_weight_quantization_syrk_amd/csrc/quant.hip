@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void colloop_kernel(
 constexpr int TKC = 32;  // K chunk
 using TrailTile = MfmaTile<128, 64, TKC, false>;
 
-__global__ __launch_bounds__(256, 2) void trailing_kernel(float* __restrict__ Wc,
+__global__ __launch_bounds__(256, 3) void trailing_kernel(float* __restrict__ Wc,
                                                        const float* __restrict__ Err,
                                                        const float* __restrict__ U,
                                                        int64_t d_out, int64_t d_in, int64_t b0,
