@@ -76,6 +76,57 @@ struct MfmaTile {
     constexpr int R = QT ? TN : K, C = QT ? K : TN;
     load_block<R, C, QPITCH>(lds + TM * PP, src, ld, rows, cols);
   }
+  // Operands of one chunk held in registers between their loads and their
+  // stores to LDS, so the next chunk's loads can be in flight while the
+  // current one multiplies.
+  static constexpr int NPR = TM * K / 256;
+  static constexpr int NQR = (QT ? TN * K : K * TN) / 256;
+  struct PQRegs {
+    float p[NPR];
+    float q[NQR];
+  };
+  // Unconditional loads from clamped addresses (rows, cols >= 1).
+  __device__ static void fetch_pq(PQRegs& v, const float* __restrict__ ps, int64_t pld,
+                                  int prows, int pcols, const float* __restrict__ qs,
+                                  int64_t qld, int qrows, int qcols) {
+    constexpr int QR = QT ? TN : K, QC = QT ? K : TN;
+#pragma unroll
+    for (int u = 0; u < NPR; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / K, c = e % K;
+      const int rc = r < prows ? r : prows - 1, cc = c < pcols ? c : pcols - 1;
+      v.p[u] = ps[(int64_t)rc * pld + cc];
+    }
+#pragma unroll
+    for (int u = 0; u < NQR; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / QC, c = e % QC;
+      const int rc = r < qrows ? r : qrows - 1, cc = c < qcols ? c : qcols - 1;
+      v.q[u] = qs[(int64_t)rc * qld + cc];
+    }
+    (void)QR;
+  }
+  // Into LDS, zero outside the valid block; NEG negates P (so products
+  // accumulate with a minus sign onto preloaded accumulators).
+  template <bool NEG>
+  __device__ static void stage_pq(float* lds, const PQRegs& v, int prows, int pcols, int qrows,
+                                  int qcols) {
+    constexpr int QC = QT ? K : TN;
+#pragma unroll
+    for (int u = 0; u < NPR; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / K, c = e % K;
+      lds[r * PP + c] = (r < prows && c < pcols) ? (NEG ? -v.p[u] : v.p[u]) : 0.0f;
+    }
+    float* lq = lds + TM * PP;
+#pragma unroll
+    for (int u = 0; u < NQR; ++u) {
+      const int e = u * 256 + threadIdx.x;
+      const int r = e / QC, c = e % QC;
+      lq[r * QPITCH + c] = (r < qrows && c < qcols) ? v.q[u] : 0.0f;
+    }
+  }
+
   // P and Q together with every load of both in flight at once (one memory
   // round trip; needs (TM*K + K*TN)/256 staging registers per thread).
   __device__ static void load_pq(float* lds, const float* __restrict__ ps, int64_t pld, int prows,

@@ -457,54 +457,66 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
   }
   const int i0 = bi * NB, j0 = bj * NB;
   const int ib = min(NB, d - i0), jb = min(NB, d - j0);
+  // The output tile is loaded into the accumulators and the products
+  // accumulate onto it with P negated on its way into LDS; step m+1's
+  // operands are loaded while step m multiplies.
   if (ltile) {
+    float* C = A + (int64_t)i0 * d + j0;
     f32x16 acc[TileT::FM][TileT::FN];
-    TileT::zero(acc);
-    for (int m = mlo; m < mhi; ++m) {
+    TileT::set_each(acc, [&](int row, int col) {
+      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < jb ? col : jb - 1)];
+    });
+    TileT::PQRegs v;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
       const int m0 = m * NB, mb = min(NB, d - m0);
+      TileT::fetch_pq(v, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
+                      A + (int64_t)j0 * d + m0, d, jb, mb);     // Q^T = L_jm
+    };
+    fetch(mlo);
+    for (int m = mlo; m < mhi; ++m) {
+      const int mb = min(NB, d - m * NB);
       if (m > mlo) __syncthreads();
-      TileT::load_pq(lds, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
-                     A + (int64_t)j0 * d + m0, d, jb, mb);       // Q^T = L_jm
+      TileT::stage_pq<true>(lds, v, ib, mb, jb, mb);
       __syncthreads();
+      if (m + 1 < mhi) fetch(m + 1);
       TileT::mma(lds, acc);
     }
     if (fuse_diag && wg == 0) {
       DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
-      float old[16];  // A_kk before this update (this workgroup's one 32 x 32 MFMA tile)
-      {
-        int n = 0;
-        TileT::for_each(acc, [&](int row, int col, float) {
-          const int r2 = row < ib ? row : ib - 1, c2 = col < ib ? col : ib - 1;
-          old[n++] = A[(int64_t)(i0 + r2) * d + j0 + c2];
-        });
-      }
       __syncthreads();  // every wave is done with the product's LDS operands
-      {
-        int n = 0;
-        TileT::for_each(acc, [&](int row, int col, float v) {
-          L.tile[row][col] = diag_entry(row, col, ib, old[n++] - v);
-        });
-      }
+      TileT::for_each(acc, [&](int row, int col, float val) {
+        L.tile[row][col] = diag_entry(row, col, ib, val);
+      });
       for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
       __syncthreads();
       diag_factor(L, A, M, Dinv, d, bi, status);
       return;
     }
-    tile_store<TileT, true>(A + (int64_t)i0 * d + j0, d, ib, jb, acc);
+    tile_store<TileT, false>(C, d, ib, jb, acc);
   } else {
     const int ms = max(mlo, bj);
     if (ms >= mhi) return;
+    float* C = M + (int64_t)i0 * d + j0;
     f32x16 acc[TileN::FM][TileN::FN];
-    TileN::zero(acc);
-    for (int m = ms; m < mhi; ++m) {
+    TileN::set_each(acc, [&](int row, int col) {
+      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < jb ? col : jb - 1)];
+    });
+    TileN::PQRegs v;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
       const int m0 = m * NB, mb = min(NB, d - m0);
+      TileN::fetch_pq(v, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
+                      M + (int64_t)m0 * d + j0, d, mb, jb);     // Q = M_mj
+    };
+    fetch(ms);
+    for (int m = ms; m < mhi; ++m) {
+      const int mb = min(NB, d - m * NB);
       if (m > ms) __syncthreads();
-      TileN::load_pq(lds, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
-                     M + (int64_t)m0 * d + j0, d, mb, jb);       // Q = M_mj
+      TileN::stage_pq<true>(lds, v, ib, mb, mb, jb);
       __syncthreads();
+      if (m + 1 < mhi) fetch(m + 1);
       TileN::mma(lds, acc);
     }
-    tile_store<TileN, true>(M + (int64_t)i0 * d + j0, d, ib, jb, acc);
+    tile_store<TileN, false>(C, d, ib, jb, acc);
   }
 }
 
