@@ -273,6 +273,36 @@ def test_quantize_parity_correlated(bits, g, sym):
     np.testing.assert_allclose(out["loss"], ref["loss_damped"], rtol=5e-3)
 
 
+@pytest.mark.parametrize("d_in,wdt", [(256, "f32"), (256, "bf16"), (100, "f32"), (100, "bf16")])
+def test_quantize_dead_columns(d_in, wdt):
+    """Channels with H_ii = 0 (inputs that never fire): prepare flags them and
+    the quantizer zeroes those columns of W before the loop ([P1] 阶段一's
+    dead-column handling), on the 8-wide and the scalar conversion paths."""
+    d_out = 48
+    H32 = _spd(d_in, 21)
+    dead_idx = np.array([0, 7, d_in // 2, d_in - 1])
+    H32[dead_idx, :] = 0.0
+    H32[:, dead_idx] = 0.0
+    rng = np.random.default_rng(22)
+    W = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    if wdt == "bf16":
+        Wb = synth.f32_to_bf16_bits(W)
+        W_dev, W64 = dev_bf16(Wb), synth.as_f64(Wb, "bf16")
+    else:
+        W_dev, W64 = dev_f32(W), W.astype(np.float64)
+    print(f"[dead] d_in={d_in} {wdt}", flush=True)
+    U, dead, status = gptq.gptq_prepare_hinv(dev_f32(np.tril(H32)))
+    out = _gpu_quant(W_dev, U, dead, 4, -1, False)
+    p = oracle.prepare(H32.astype(np.float64))
+    assert dead.cpu().numpy().astype(bool).tolist() == p["dead"].tolist()
+    ref = oracle.gptq(W64, p["U"], p["dead"], bits=4, group_size=-1, sym=False, block=128)
+    rep = compare_quant(out, ref, group_size=-1, bits=4, W=W64, H0=H32.astype(np.float64))
+    print(f"[dead] {rep}", flush=True)
+    # a dead column quantizes the zero it was set to
+    deq = out["scales"][:, :1] * (out["codes"][:, dead_idx].astype(np.float64) - out["zeros"][:, :1])
+    np.testing.assert_array_equal(deq, 0.0)
+
+
 def test_quantize_empty_rows():
     U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(2 * np.eye(128)))
     W = torch.zeros((0, 128), dtype=torch.float32, device=DEV)
