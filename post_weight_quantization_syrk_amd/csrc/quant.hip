@@ -25,6 +25,7 @@ namespace {
 
 constexpr int QB = 128;      // block width (columns)
 constexpr int UPITCH = 132;  // LDS pitch (floats) of the U block in the column loop
+constexpr int QG = 2;        // blocks per far trailing update
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -318,30 +319,31 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:]  (fp32 MFMA, 128 x 64 tiles).
-// The tile of Wc is loaded into the accumulators first and the error operand
-// is negated on its way into LDS, so the products accumulate onto Wc and the
-// final store needs no read.  K runs in chunks of 32 through 46 KiB of LDS,
-// the next chunk's loads in flight while the current one multiplies; two
-// workgroups share a CU, one's loads and stores overlapping the other's
-// matrix products.
+// Wc[:, n0:n1] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:n1]  (fp32 MFMA, TM x 64
+// tiles).  The tile of Wc is loaded into the accumulators first and the error
+// operand is negated on its way into LDS, so the products accumulate onto Wc
+// and the final store needs no read.  K runs in chunks of 32 (29 KiB of LDS
+// for TM = 128), the next chunk's loads in flight while the current one
+// multiplies; three workgroups share a CU, one's loads and stores overlapping
+// the others' matrix products.
 constexpr int TKC = 32;  // K chunk
-using TrailTile = MfmaTile<128, 64, TKC, false>;
 
+template <int TM>
 __global__ __launch_bounds__(256, 3) void trailing_kernel(float* __restrict__ Wc,
                                                        const float* __restrict__ Err,
                                                        const float* __restrict__ U,
                                                        int64_t d_out, int64_t d_in, int64_t b0,
-                                                       int kb, int64_t n0) {
-  constexpr int TM = 128, TN = 64;
+                                                       int kb, int64_t n0, int64_t n1) {
+  constexpr int TN = 64;
+  using TrailTile = MfmaTile<TM, TN, TKC, false>;
   constexpr int NP = TM * TKC / 256, NQ = TKC * TN / 256;
   __shared__ __attribute__((aligned(16))) float lds[TrailTile::lds_floats];
-  const int64_t ncols = d_in - n0;
+  const int64_t ncols = n1 - n0;
   const int ntn = (int)ceil_div(ncols, TN);
   const int64_t m0 = (int64_t)(blockIdx.x / ntn) * TM;
   const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * TN;
   const int rows = (int)min<int64_t>(TM, d_out - m0);
-  const int cols = (int)min<int64_t>(TN, d_in - n0t);
+  const int cols = (int)min<int64_t>(TN, n1 - n0t);
   f32x16 acc[TrailTile::FM][TrailTile::FN];
   float* C = Wc + m0 * d_in + n0t;
   // the tile of Wc into the accumulators (clamped addresses; masked at the store)
@@ -450,16 +452,31 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
   if (q.gsize == 0)
     hipLaunchKernelGGL(rowparams_kernel, dim3((unsigned)ceil_div(d_out, 4)), dim3(256), 0, stream,
                        (const float*)w.Wc, d_out, d_in, q, scales, zeros);
+  // Blocks in groups of QG: after each block's column loop its errors go to
+  // the rest of its group only (near update, K = 128); after the group, all
+  // of the group's errors go to the columns after it at once (far update,
+  // K = 128 QG), so the bulk of W is read and written once per group.
   const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
-  for (int64_t b0 = 0; b0 < d_in; b0 += QB) {
-    hipLaunchKernelGGL(colloop_kernel, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err, U, d_out,
-                       d_in, b0, q, codes, scales, zeros, loss_rows);
-    const int kb = (int)std::min<int64_t>(QB, d_in - b0);
-    const int64_t n0 = b0 + kb;
-    if (n0 < d_in) {
-      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - n0, 64);
-      hipLaunchKernelGGL(trailing_kernel, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
-                         (const float*)w.Err, U, d_out, d_in, b0, kb, n0);
+  const int64_t nb = ceil_div(d_in, QB);
+  for (int64_t g0 = 0; g0 < nb; g0 += QG) {
+    const int64_t gend = std::min<int64_t>(nb, g0 + QG);
+    const int64_t gcol = std::min<int64_t>(d_in, gend * QB);  // first column after the group
+    for (int64_t b = g0; b < gend; ++b) {
+      const int64_t b0 = b * QB;
+      hipLaunchKernelGGL(colloop_kernel, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err, U,
+                         d_out, d_in, b0, q, codes, scales, zeros, loss_rows);
+      const int64_t n0 = b0 + QB;
+      if (b + 1 < gend) {  // blocks before the group's last are full
+        const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
+        hipLaunchKernelGGL(trailing_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, stream,
+                           w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
+      }
+    }
+    if (gcol < d_in) {  // every block of the group is full
+      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
+      hipLaunchKernelGGL(trailing_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
+                         (const float*)w.Err, U, d_out, d_in, g0 * QB, (int)(gcol - g0 * QB),
+                         gcol, d_in);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
