@@ -10,8 +10,12 @@
 //              (DPP row broadcast), every lane takes the same rounding decision,
 //              and each lane applies the feedback to its own 8 columns.  Group
 //              min/max come from a 16-lane butterfly at the group's first column.
-//   trailing : W[:, next blocks] -= Err_blk U[blk, next blocks], an fp32 MFMA
-//              GEMM (v_mfma_f32_32x32x2f32), K = 128.
+//   trailing : W[:, later columns] -= Err U, an fp32 MFMA GEMM
+//              (v_mfma_f32_32x32x2f32).  Blocks go in groups of four: after
+//              each block, its errors update the rest of its group (K = 128);
+//              after the group, all four blocks' errors update every column
+//              after it at once (K = 512), so the bulk of W is read and
+//              written once per group.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_f32.h"
@@ -25,7 +29,7 @@ namespace {
 
 constexpr int QB = 128;      // block width (columns)
 constexpr int UPITCH = 132;  // LDS pitch (floats) of the U block in the column loop
-constexpr int QG = 2;        // blocks per far trailing update
+constexpr int QG = 4;        // blocks per far trailing update
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
