@@ -245,6 +245,30 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
 #pragma unroll
         for (int i = 0; i < 4; ++i) rbuf[r0 + i][c] = acc[i];
       }
+      // The deferred part of the previous sub-step's rank-16 update: rows
+      // i >= s0 + 16, columns s0 <= j <= i (its block-s part ran before this
+      // sub-step).  pan still holds the previous sub-step's panel.  Nothing
+      // here touches block s, which wave 0 is factoring.
+      constexpr int drows = NB - s0 - SB, dcols = NB - s0;
+      if constexpr (drows > 0) {
+        for (int q = e; q < drows * dcols; q += 192) {
+          const int i = s0 + SB + q / dcols, jj = s0 + q % dcols;
+          if (jj <= i) {
+            const float4* pi = (const float4*)pan[i];
+            const float4* pj = (const float4*)pan[jj];
+            float acc = 0.0f;
+#pragma unroll
+            for (int u = 0; u < SB / 4; ++u) {
+              const float4 x = pi[u], y = pj[u];
+              acc = fmaf(x.x, y.x, acc);
+              acc = fmaf(x.y, y.y, acc);
+              acc = fmaf(x.z, y.z, acc);
+              acc = fmaf(x.w, y.w, acc);
+            }
+            tile[i][jj] -= acc;
+          }
+        }
+      }
     }
     __syncthreads();
     // ---------------- B
@@ -288,9 +312,14 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
     }
     __syncthreads();
     // ---------------- C
+    // The rank-16 update A_{i,j} -= L_{i,S} L_{j,S}^T on the next diagonal
+    // block only (rows and columns s0+16 .. s0+31, one element per thread):
+    // that is all the next sub-step's pivots need.  The rest of the update
+    // (rows below it) runs on waves 1-3 while wave 0 factors that block.
     if constexpr (rows > 0) {
-      for (int e = t; e < rows * rows; e += 256) {
-        const int i = s0 + SB + e / rows, jj = s0 + SB + e % rows;
+      {
+        const int e = t;
+        const int i = s0 + SB + (e >> 4), jj = s0 + SB + (e & 15);
         if (jj <= i) {
           const float4* pi = (const float4*)pan[i];
           const float4* pj = (const float4*)pan[jj];
