@@ -276,14 +276,23 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
     //   L[i][s0+j] = sum_q A[i][s0+q] M_SS[j][q]   (M_SS[j][q] = 0 for q > j).
     // Threads [4 rows, 4 rows + 4 s0): row block of L^{-1}, column c, rows
     //   4g..4g+3:  M[s0+r][c] = -sum_p M_SS[r][p] R[p][c]   (M_SS[r][p] = 0 for p > r).
-    float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    // A panel row is read and written only by its own four threads, which
+    // are lanes of one wave (their reads all precede their writes), and the
+    // L^{-1} row block writes columns < s0, which nobody reads here: one
+    // barrier at the end suffices.
     if (t < 4 * rows) {
       const int i = s0 + SB + (t >> 2), j0 = 4 * (t & 3);
+      float pv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int q = 0; q < SB; ++q) {
         const float av = tile[i][s0 + q];
 #pragma unroll
         for (int u = 0; u < 4; ++u) pv[u] = fmaf(av, mtile[s0 + j0 + u][s0 + q], pv[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tile[i][s0 + j0 + u] = pv[u];
+        pan[i][j0 + u] = pv[u];
       }
     }
     if constexpr (s > 0) {
@@ -299,15 +308,6 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) mtile[s0 + g0 + u][c] = -acc[u];
-      }
-    }
-    __syncthreads();  // every read of the panel's A values is done
-    if (t < 4 * rows) {
-      const int i = s0 + SB + (t >> 2), j0 = 4 * (t & 3);
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tile[i][s0 + j0 + u] = pv[u];
-        pan[i][j0 + u] = pv[u];
       }
     }
     __syncthreads();
