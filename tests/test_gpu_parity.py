@@ -129,7 +129,7 @@ def _spd(d, seed, n=None):
     return (2.0 * x.T @ x).astype(np.float32)
 
 
-@pytest.mark.parametrize("d", [1, 5, 64, 100, 130, 256, 1000])
+@pytest.mark.parametrize("d", [1, 5, 64, 100, 130, 256, 1000, 2150, 4096])
 def test_prepare_matches_oracle(d):
     H32 = _spd(d, d)
     H = dev_f32(np.tril(H32))
@@ -137,8 +137,13 @@ def test_prepare_matches_oracle(d):
     ref = oracle.prepare(H32.astype(np.float64), 0.01)
     Ug = U.cpu().numpy().astype(np.float64)
     err = np.max(np.abs(Ug - ref["U"])) / np.max(np.abs(ref["U"]))
-    print(f"[prepare] d={d} max rel U err {err:.2e}", flush=True)
-    assert err <= 2e-6
+    # fp32 bar: U's entries come out of O(d)-long chains of rounded fp32
+    # products (factorization, then triangular inverse); with independent
+    # rounding errors the relative error grows like sqrt(d) * u (u = 2^-24),
+    # so the bar is that, with 2e-6 as the floor for small d.
+    bar = max(2e-6, np.sqrt(d) * 2.0**-24)
+    print(f"[prepare] d={d} max rel U err {err:.2e} (bar {bar:.2e})", flush=True)
+    assert err <= bar
     assert np.all(np.tril(Ug, -1) == 0)
     np.testing.assert_allclose(H.cpu().numpy(), ref["H"], rtol=2e-7, atol=0)
     assert not dead.cpu().numpy().any()
