@@ -34,6 +34,7 @@ struct MfmaTile {
   static constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(WM % 32 == 0 && WN % 32 == 0 && K % 2 == 0, "tile shape");
   static constexpr size_t lds_floats = (size_t)TM * PP + (size_t)QROWS * QPITCH;
+  static constexpr int lds_q_offset = TM * PP;  // where the Q operand starts in LDS
 
   // Copy an R x C block (rows x cols valid, zero-padded) from row-major global
   // memory into LDS with the given pitch.  Loads are unconditional (addresses

@@ -6,12 +6,17 @@
 // and factorizing again, it is formed as U = V^{-1} with H = V V^T, V upper: in
 // the index-reversed space A = J H J (J reverses the order) this is an ordinary
 // Cholesky A = L L^T and a triangular inverse M = L^{-1}, and U = J M J.  Both
-// run blocked (64 x 64 blocks) in fp32, right-looking, fused per step:
+// run blocked (64 x 64 blocks) in fp32, right-looking, per step k:
 //   diag   : L_kk = chol(A_kk) and its inverse, one workgroup;
 //   panel  : L_ik = A_ik L_kk^{-T} (i > k) and M_kj = L_kk^{-1} B_kj (j < k);
 //   update : A_ij -= L_ik L_jk^T (i >= j > k) and B_ij -= L_ik M_kj (i > k >= j),
-// where B accumulates the right-hand side of L M = I.  Panel and update tiles
-// are fp32 MFMA products (v_mfma_f32_32x32x2f32).
+// where B accumulates the right-hand side of L M = I.  Steps go in groups of
+// UG: inside a group only the next block column (and block row of B) is
+// brought up to date before each step (fac_colupd_kernel, which also applies
+// the previous step's panel), and after the group the whole trailing part
+// receives the group's panels at once (fac_update_kernel).  The workgroup
+// that updates the next diagonal block factorizes it in the same launch.
+// Panel and update tiles are fp32 MFMA products (v_mfma_f32_32x32x2f32).
 #include "common.h"
 #include "kernels.h"
 #include "mfma_f32.h"
@@ -30,7 +35,7 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 struct PrepWs {
   float* A;      // [d x d] reversed damped H, then L (lower)
   float* M;      // [d x d] right-hand side / L^{-1} (lower)
-  float* Dinv;   // [NB x NB] inverse of the current diagonal block
+  float* Dinv[2];  // [NB x NB] inverse of the diagonal block of step k, in Dinv[k % 2]
   double* scal;  // [0] = lambda
 };
 
@@ -40,8 +45,9 @@ PrepWs carve(void* ws, int64_t d) {
   const size_t mat = align256((size_t)d * d * sizeof(float));
   w.A = (float*)p;
   w.M = (float*)(p + mat);
-  w.Dinv = (float*)(p + 2 * mat);
-  w.scal = (double*)(p + 2 * mat + align256(NB * NB * sizeof(float)));
+  w.Dinv[0] = (float*)(p + 2 * mat);
+  w.Dinv[1] = (float*)(p + 2 * mat + align256(NB * NB * sizeof(float)));
+  w.scal = (double*)(p + 2 * mat + 2 * align256(NB * NB * sizeof(float)));
   return w;
 }
 
@@ -434,25 +440,20 @@ __global__ __launch_bounds__(256) void fac_panel_kernel(float* __restrict__ A,
   }
 }
 
-// Updates of both factorizations by the panels of steps m in [mlo, mhi)
-// (delayed, grouped updates: the trailing matrix is read and written once per
-// group of steps instead of once per step):
-//   L tiles  A_ij -= sum_m L_im L_jm^T
-//   M tiles  B_ij -= sum_m L_im M_mj   (only m >= j contributes: M is lower)
-// PART 1 (before step kc of a group, mhi = kc): block column kc of L (tiles
-//   (i, kc), i >= kc) and block row kc of B (tiles (kc, j), j < kc) -- what
-//   the diagonal and panel kernels of step kc read;
-// PART 2 (after the group, mhi = its end): L tiles (i, j) with i >= j >= mhi
-//   and B tiles (i, j) with i >= mhi, j < mhi.
+// After a group of steps [mlo, mhi) (delayed, grouped updates: the trailing
+// matrix is read and written once per group of steps instead of once per
+// step), both factorizations receive the group's panels:
+//   L tiles  A_ij -= sum_m L_im L_jm^T   (i >= j >= mhi)
+//   M tiles  B_ij -= sum_m L_im M_mj     (i >= mhi, j < mhi; only m >= j
+//                                         contributes: M is lower)
 // Each step m is one K = 64 chunk through LDS, accumulated in registers.
 // With fuse_diag, workgroup 0 -- the one that updates the next diagonal
-// block (block mhi: tile (mhi, mhi) comes first in both parts) -- goes on to
-// factorize it: the updated block goes from its accumulators straight into the
-// factorization's LDS copies, and the factorization runs while the other
-// workgroups finish their tiles, instead of as a kernel of its own after them.
-// (It touches only block (mhi, mhi) of A and M and Dinv, which no other tile
-// of this launch reads.)
-template <int PART>
+// block (tile (mhi, mhi) comes first) -- goes on to factorize it: the
+// updated block goes from its accumulators straight into the factorization's
+// LDS copies, and the factorization runs while the other workgroups finish
+// their tiles, instead of as a kernel of its own after them.  (It touches
+// only block (mhi, mhi) of A and M and Dinv, which no other tile of this
+// launch reads.)
 __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
                                                          float* __restrict__ M,
                                                          float* __restrict__ Dinv, int d, int nb,
@@ -462,27 +463,19 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
   constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
   __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
   const int wg = blockIdx.x;
-  bool ltile;
+  const int T = nb - mhi;
+  const int ta = T * (T + 1) / 2;
+  const bool ltile = wg < ta;
   int bi, bj;  // output block coordinates
-  if (PART == 1) {
-    const int T = nb - mhi;
-    ltile = wg < T;
-    bi = ltile ? mhi + wg : mhi;
-    bj = ltile ? mhi : wg - T;
+  if (ltile) {
+    int ii, jj;
+    tri_coords(wg, ii, jj);
+    bi = mhi + ii;
+    bj = mhi + jj;
   } else {
-    const int T = nb - mhi;
-    const int ta = T * (T + 1) / 2;
-    ltile = wg < ta;
-    if (ltile) {
-      int ii, jj;
-      tri_coords(wg, ii, jj);
-      bi = mhi + ii;
-      bj = mhi + jj;
-    } else {
-      const int idx = wg - ta;
-      bi = mhi + idx / mhi;
-      bj = idx % mhi;
-    }
+    const int idx = wg - ta;
+    bi = mhi + idx / mhi;
+    bj = idx % mhi;
   }
   const int i0 = bi * NB, j0 = bj * NB;
   const int ib = min(NB, d - i0), jb = min(NB, d - j0);
@@ -549,6 +542,143 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
   }
 }
 
+// Part 1 of step kc (g0 < kc < group end) with step p = kc - 1's panel folded
+// in, so no panel launch sits between the two diagonal factorizations:
+//   L tile (i, kc), i >= kc:  P_i = A_ip Dinv_p^T (stored: the panel block
+//     L_ip) and P_k = A_kc,p Dinv_p^T (recomputed by every workgroup), then
+//     A_i,kc -= sum_{m in [g0, p)} L_im L_kc,m^T + P_i P_k^T;
+//   B tile (kc, j), j < kc:   for j < p, M_pj = Dinv_p B_pj (stored: the
+//     panel's block of L^{-1}); M_pp = Dinv_p; then
+//     B_kc,j -= sum_{m in [max(g0, j), p)} L_kc,m M_mj + P_k M_pj.
+// The output tile is preloaded into the accumulators and the products
+// accumulate onto it with P negated.  Workgroup 0 (tile (kc, kc)) then
+// factorizes the diagonal block, as in fac_update_kernel, into Dinv_out (the
+// other buffer: the others read Dinv_p throughout).  Block p is never the
+// last block, so it is a full one.
+__global__ __launch_bounds__(256) void fac_colupd_kernel(float* __restrict__ A,
+                                                         float* __restrict__ M,
+                                                         const float* __restrict__ Dinv,
+                                                         float* __restrict__ Dinv_out, int d,
+                                                         int nb, int g0, int kc,
+                                                         int32_t* status) {
+  if (*status != 0) return;
+  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+  const int p = kc - 1, p0 = p * NB, kc0 = kc * NB;
+  const int kcb = min(NB, d - kc0);
+  const int wg = blockIdx.x, T = nb - kc;
+  const float* Akp = A + (int64_t)kc0 * d + p0;
+  // acc = (rows x 64 block at src) * Dinv_p^T
+  auto panel_t = [&](f32x16 (&acc)[TileT::FM][TileT::FN], const float* src, int rows)
+      __attribute__((always_inline)) {
+    TileT::zero(acc);
+    TileT::load_p(lds, src, d, rows, NB);
+    TileT::load_q(lds, Dinv, NB, NB, NB);  // Q^T = Dinv_p
+    __syncthreads();
+    TileT::mma(lds, acc);
+    __syncthreads();  // LDS free again
+  };
+  if (wg < T) {
+    const int i = kc + wg, i0 = i * NB, ib = min(NB, d - i0);
+    f32x16 pi[TileT::FM][TileT::FN], pk[TileT::FM][TileT::FN];
+    panel_t(pi, A + (int64_t)i0 * d + p0, ib);
+    if (wg == 0) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pk[0][0][r] = pi[0][0][r];
+    } else {
+      panel_t(pk, Akp, kcb);
+    }
+    // L_ip, for the rows below kc (row kc's is used only here, and every
+    // workgroup reads row kc's A_kc,p, so it stays as it is)
+    if (wg != 0) tile_store<TileT, false>(A + (int64_t)i0 * d + p0, d, ib, NB, pi);
+    float* C = A + (int64_t)i0 * d + kc0;
+    f32x16 acc[TileT::FM][TileT::FN];
+    TileT::set_each(acc, [&](int row, int col) {
+      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < kcb ? col : kcb - 1)];
+    });
+    TileT::PQRegs v;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
+      TileT::fetch_pq(v, A + (int64_t)i0 * d + m * NB, d, ib, NB,   // P = L_im
+                      A + (int64_t)kc0 * d + m * NB, d, kcb, NB);   // Q^T = L_kc,m
+    };
+    if (g0 < p) fetch(g0);
+    for (int m = g0; m < p; ++m) {
+      if (m > g0) __syncthreads();
+      TileT::stage_pq<true>(lds, v, ib, NB, kcb, NB);
+      __syncthreads();
+      if (m + 1 < p) fetch(m + 1);
+      TileT::mma(lds, acc);
+    }
+    // step p from registers: P = -P_i, Q^T = P_k
+    __syncthreads();
+    TileT::for_each(pi, [&](int row, int col, float x) { lds[row * TileT::PP + col] = -x; });
+    TileT::for_each(pk, [&](int row, int col, float x) {
+      lds[TileT::lds_q_offset + row * TileT::QPITCH + col] = x;
+    });
+    __syncthreads();
+    TileT::mma(lds, acc);
+    if (wg == 0) {
+      DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
+      __syncthreads();  // every wave is done with the product's LDS operands
+      TileT::for_each(acc, [&](int row, int col, float val) {
+        L.tile[row][col] = diag_entry(row, col, ib, val);
+      });
+      for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
+      __syncthreads();
+      diag_factor(L, A, M, Dinv_out, d, kc, status);
+      return;
+    }
+    tile_store<TileT, false>(C, d, ib, kcb, acc);
+  } else {
+    const int j = wg - T, j0 = j * NB;  // full block, j < kc
+    f32x16 mpj[TileN::FM][TileN::FN];
+    if (j < p) {
+      TileN::zero(mpj);
+      TileN::load_p(lds, Dinv, NB, NB, NB);
+      TileN::load_q(lds, M + (int64_t)p0 * d + j0, d, NB, NB);  // B_pj
+      __syncthreads();
+      TileN::mma(lds, mpj);
+      __syncthreads();
+      tile_store<TileN, false>(M + (int64_t)p0 * d + j0, d, NB, NB, mpj);  // M_pj
+    }
+    f32x16 pk[TileT::FM][TileT::FN];
+    panel_t(pk, Akp, kcb);
+    float* C = M + (int64_t)kc0 * d + j0;
+    f32x16 acc[TileN::FM][TileN::FN];
+    TileN::set_each(acc, [&](int row, int col) {
+      return C[(int64_t)(row < kcb ? row : kcb - 1) * d + col];
+    });
+    const int ms = max(g0, j);
+    TileN::PQRegs v;
+    auto fetch = [&](int m) __attribute__((always_inline)) {
+      TileN::fetch_pq(v, A + (int64_t)kc0 * d + m * NB, d, kcb, NB,   // P = L_kc,m
+                      M + (int64_t)m * NB * d + j0, d, NB, NB);       // Q = M_mj
+    };
+    if (ms < p) fetch(ms);
+    for (int m = ms; m < p; ++m) {
+      if (m > ms) __syncthreads();
+      TileN::stage_pq<true>(lds, v, kcb, NB, NB, NB);
+      __syncthreads();
+      if (m + 1 < p) fetch(m + 1);
+      TileN::mma(lds, acc);
+    }
+    // step p: P = -P_k, Q = M_pj (Dinv_p itself when j = p)
+    __syncthreads();
+    TileT::for_each(pk, [&](int row, int col, float x) { lds[row * TileN::PP + col] = -x; });
+    if (j < p) {
+      TileN::for_each(mpj, [&](int row, int col, float x) {
+        lds[TileN::lds_q_offset + row * TileN::QPITCH + col] = x;
+      });
+    } else {
+      for (int e = threadIdx.x; e < NB * NB; e += 256)
+        lds[TileN::lds_q_offset + (e / NB) * TileN::QPITCH + e % NB] = Dinv[e];
+    }
+    __syncthreads();
+    TileN::mma(lds, acc);
+    tile_store<TileN, false>(C, d, kcb, NB, acc);
+  }
+}
+
 // U[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
 __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ M,
                                                       float* __restrict__ U, int d) {
@@ -563,7 +693,7 @@ __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ 
 }  // namespace
 
 size_t prepare_workspace(int64_t d) {
-  return 2 * align256((size_t)d * d * sizeof(float)) + align256(NB * NB * sizeof(float)) + 256;
+  return 2 * align256((size_t)d * d * sizeof(float)) + 2 * align256(NB * NB * sizeof(float)) + 256;
 }
 
 hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t* dead,
@@ -587,23 +717,27 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
     for (int k = g0; k < gend; ++k) {
       // the diagonal block of step k is factorized by the update launch that
       // brings it up to date (this group's part 1, or the previous group's
-      // part 2); only step 0 needs a launch of its own
+      // part 2); only step 0 needs a launch of its own.  Part 1 also applies
+      // the previous step's panel, so only a group's last step has a panel
+      // launch.
       if (k > g0)
-        hipLaunchKernelGGL(fac_update_kernel<1>, dim3(nb - k + k), dim3(256), 0, stream, w.A, w.M,
-                           w.Dinv, d, nb, g0, k, 1, dev_status);
-      else if (k == 0)
-        hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv, d, k,
+        hipLaunchKernelGGL(fac_colupd_kernel, dim3(nb), dim3(256), 0, stream, w.A, w.M,
+                           (const float*)w.Dinv[(k - 1) & 1], w.Dinv[k & 1], d, nb, g0, k,
                            dev_status);
+      else if (k == 0)
+        hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv[0], d,
+                           k, dev_status);
+      if (k + 1 < gend) continue;
       const int nrow = nb - k - 1;
       if (nrow + k > 0)
         hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
-                           (const float*)w.Dinv, d, k, nrow, (const int32_t*)dev_status);
+                           (const float*)w.Dinv[k & 1], d, k, nrow, (const int32_t*)dev_status);
     }
     const int T = nb - gend;
     const int tiles = T * (T + 1) / 2 + T * gend;
     if (tiles > 0)
-      hipLaunchKernelGGL(fac_update_kernel<2>, dim3(tiles), dim3(256), 0, stream, w.A, w.M,
-                         w.Dinv, d, nb, g0, gend, 1, dev_status);
+      hipLaunchKernelGGL(fac_update_kernel, dim3(tiles), dim3(256), 0, stream, w.A, w.M,
+                         w.Dinv[gend & 1], d, nb, g0, gend, 1, dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
