@@ -13,9 +13,12 @@
 // where B accumulates the right-hand side of L M = I.  Steps go in groups of
 // UG: inside a group only the next block column (and block row of B) is
 // brought up to date before each step (fac_colupd_kernel, which also applies
-// the previous step's panel), and after the group the whole trailing part
-// receives the group's panels at once (fac_update_kernel).  The workgroup
-// that updates the next diagonal block factorizes it in the same launch.
+// the previous step's panel), and after the group the trailing part receives
+// the group's panels in two pieces: the band the next group's steps read
+// (fac_update_kernel, whose workgroup on the next diagonal block factorizes it
+// in the same launch), and the rest through extra workgroups of the next
+// group's column-update launches, which by themselves leave most of the chip
+// idle.
 // Panel and update tiles are fp32 MFMA products (v_mfma_f32_32x32x2f32).
 #include "common.h"
 #include "kernels.h"
@@ -447,36 +450,13 @@ __global__ __launch_bounds__(256) void fac_panel_kernel(float* __restrict__ A,
 //   M tiles  B_ij -= sum_m L_im M_mj     (i >= mhi, j < mhi; only m >= j
 //                                         contributes: M is lower)
 // Each step m is one K = 64 chunk through LDS, accumulated in registers.
-// With fuse_diag, workgroup 0 -- the one that updates the next diagonal
-// block (tile (mhi, mhi) comes first) -- goes on to factorize it: the
-// updated block goes from its accumulators straight into the factorization's
-// LDS copies, and the factorization runs while the other workgroups finish
-// their tiles, instead of as a kernel of its own after them.  (It touches
-// only block (mhi, mhi) of A and M and Dinv, which no other tile of this
-// launch reads.)
-__global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
-                                                         float* __restrict__ M,
-                                                         float* __restrict__ Dinv, int d, int nb,
-                                                         int mlo, int mhi, int fuse_diag,
-                                                         int32_t* status) {
-  if (*status != 0) return;
-  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
-  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
-  const int wg = blockIdx.x;
-  const int T = nb - mhi;
-  const int ta = T * (T + 1) / 2;
-  const bool ltile = wg < ta;
-  int bi, bj;  // output block coordinates
-  if (ltile) {
-    int ii, jj;
-    tri_coords(wg, ii, jj);
-    bi = mhi + ii;
-    bj = mhi + jj;
-  } else {
-    const int idx = wg - ta;
-    bi = mhi + idx / mhi;
-    bj = idx % mhi;
-  }
+// One output tile (block bi, bj) per call; with diag (tile (mhi, mhi) only)
+// the updated block goes from its accumulators straight into the diagonal
+// factorization's LDS copies and is factorized into Dinv instead of stored.
+__device__ __forceinline__ void update_tile(float* __restrict__ A, float* __restrict__ M,
+                                            float* __restrict__ Dinv, float* lds, int d,
+                                            int mlo, int mhi, bool ltile, int bi, int bj,
+                                            bool diag, int32_t* status) {
   const int i0 = bi * NB, j0 = bj * NB;
   const int ib = min(NB, d - i0), jb = min(NB, d - j0);
   // The output tile is loaded into the accumulators and the products
@@ -503,7 +483,7 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
       if (m + 1 < mhi) fetch(m + 1);
       TileT::mma(lds, acc);
     }
-    if (fuse_diag && wg == 0) {
+    if (diag) {
       DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
       __syncthreads();  // every wave is done with the product's LDS operands
       TileT::for_each(acc, [&](int row, int col, float val) {
@@ -542,6 +522,71 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
   }
 }
 
+// The tiles a group's update touches split in two.  The band -- L block
+// columns [mhi, mhi + UG) and B block rows [mhi, mhi + UG), what the next
+// group's steps read -- is updated right after the group (fac_update_kernel).
+// The rest -- L block columns and B block rows from mhi + UG on -- is read by
+// nothing until the next group's own update, and is updated meanwhile by
+// extra workgroups of the next group's column-update launches, on the compute
+// units those latency-bound launches leave idle.  The two sets are disjoint
+// from each other and from everything the next group's column updates and
+// panel read or write.
+__host__ __device__ inline int band_ltiles(int nb, int c0, int c1) {
+  return (c1 - c0) * nb - (c0 + c1 - 1) * (c1 - c0) / 2;
+}
+__host__ __device__ inline int band_tiles(int nb, int mhi) {
+  const int c1 = min(nb, mhi + UG);
+  return band_ltiles(nb, mhi, c1) + (c1 - mhi) * mhi;
+}
+__host__ __device__ inline int rest_tiles(int nb, int mhi) {
+  const int T = nb - (mhi + UG);
+  return T > 0 ? T * (T + 1) / 2 + T * mhi : 0;
+}
+
+// Band tile t: L tiles column by column from (mhi, mhi) down, then the B
+// tiles row by row.  Workgroup 0 (tile (mhi, mhi)) also factorizes the next
+// diagonal block into Dinv: it touches only block (mhi, mhi) of A and M and
+// Dinv, which no other tile of this launch reads.
+__global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
+                                                         float* __restrict__ M,
+                                                         float* __restrict__ Dinv, int d, int nb,
+                                                         int mlo, int mhi, int32_t* status) {
+  if (*status != 0) return;
+  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+  const int c1 = min(nb, mhi + UG);
+  int t = blockIdx.x;
+  const int nl = band_ltiles(nb, mhi, c1);
+  if (t < nl) {
+    int bj = mhi;
+    while (t >= nb - bj) {
+      t -= nb - bj;
+      ++bj;
+    }
+    update_tile(A, M, Dinv, lds, d, mlo, mhi, true, bj + t, bj, blockIdx.x == 0, status);
+  } else {
+    t -= nl;
+    update_tile(A, M, Dinv, lds, d, mlo, mhi, false, mhi + t / mhi, t % mhi, false, status);
+  }
+}
+
+// Rest tile t of the group [mhi - UG, mhi): the L triangle from block mhi + UG
+// row by row, then the B tiles row by row.
+__device__ __forceinline__ void rest_tile(float* __restrict__ A, float* __restrict__ M,
+                                          float* lds, int d, int nb, int mhi, int t,
+                                          int32_t* status) {
+  const int c0 = mhi + UG, T = nb - c0, ta = T * (T + 1) / 2;
+  if (t < ta) {
+    int ii, jj;
+    tri_coords(t, ii, jj);
+    update_tile(A, M, nullptr, lds, d, mhi - UG, mhi, true, c0 + ii, c0 + jj, false, status);
+  } else {
+    t -= ta;
+    update_tile(A, M, nullptr, lds, d, mhi - UG, mhi, false, c0 + t / mhi, t % mhi, false,
+                status);
+  }
+}
+
 // Part 1 of step kc (g0 < kc < group end) with step p = kc - 1's panel folded
 // in, so no panel launch sits between the two diagonal factorizations:
 //   L tile (i, kc), i >= kc:  P_i = A_ip Dinv_p^T (stored: the panel block
@@ -555,15 +600,19 @@ __global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
 // factorizes the diagonal block, as in fac_update_kernel, into Dinv_out (the
 // other buffer: the others read Dinv_p throughout).  Block p is never the
 // last block, so it is a full one.
-__global__ __launch_bounds__(256) void fac_colupd_kernel(float* __restrict__ A,
+__global__ __launch_bounds__(256, 2) void fac_colupd_kernel(float* __restrict__ A,
                                                          float* __restrict__ M,
                                                          const float* __restrict__ Dinv,
                                                          float* __restrict__ Dinv_out, int d,
-                                                         int nb, int g0, int kc,
+                                                         int nb, int g0, int kc, int rest_lo,
                                                          int32_t* status) {
   if (*status != 0) return;
   constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
   __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+  if ((int)blockIdx.x >= nb) {  // the previous group's rest tiles
+    rest_tile(A, M, lds, d, nb, g0, rest_lo + (int)blockIdx.x - nb, status);
+    return;
+  }
   const int p = kc - 1, p0 = p * NB, kc0 = kc * NB;
   const int kcb = min(NB, d - kc0);
   const int wg = blockIdx.x, T = nb - kc;
@@ -714,30 +763,35 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
   const int nb = (int)ceil_div(d, NB);
   for (int g0 = 0; g0 < nb; g0 += UG) {
     const int gend = std::min(nb, g0 + UG);
+    // the previous group's rest tiles, spread evenly over this group's column
+    // updates (there are UG - 1 of them whenever the rest is not empty)
+    const int rest = g0 > 0 ? rest_tiles(nb, g0) : 0;
+    const int share = (int)ceil_div(rest, UG - 1);
     for (int k = g0; k < gend; ++k) {
       // the diagonal block of step k is factorized by the update launch that
       // brings it up to date (this group's part 1, or the previous group's
       // part 2); only step 0 needs a launch of its own.  Part 1 also applies
       // the previous step's panel, so only a group's last step has a panel
       // launch.
-      if (k > g0)
-        hipLaunchKernelGGL(fac_colupd_kernel, dim3(nb), dim3(256), 0, stream, w.A, w.M,
-                           (const float*)w.Dinv[(k - 1) & 1], w.Dinv[k & 1], d, nb, g0, k,
+      if (k > g0) {
+        const int lo = std::min(rest, (k - g0 - 1) * share);
+        const int n = std::min(rest, lo + share) - lo;
+        hipLaunchKernelGGL(fac_colupd_kernel, dim3(nb + n), dim3(256), 0, stream, w.A, w.M,
+                           (const float*)w.Dinv[(k - 1) & 1], w.Dinv[k & 1], d, nb, g0, k, lo,
                            dev_status);
-      else if (k == 0)
+      } else if (k == 0) {
         hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv[0], d,
                            k, dev_status);
+      }
       if (k + 1 < gend) continue;
       const int nrow = nb - k - 1;
       if (nrow + k > 0)
         hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
                            (const float*)w.Dinv[k & 1], d, k, nrow, (const int32_t*)dev_status);
     }
-    const int T = nb - gend;
-    const int tiles = T * (T + 1) / 2 + T * gend;
-    if (tiles > 0)
-      hipLaunchKernelGGL(fac_update_kernel, dim3(tiles), dim3(256), 0, stream, w.A, w.M,
-                         w.Dinv[gend & 1], d, nb, g0, gend, 1, dev_status);
+    if (gend < nb)
+      hipLaunchKernelGGL(fac_update_kernel, dim3(band_tiles(nb, gend)), dim3(256), 0, stream,
+                         w.A, w.M, w.Dinv[gend & 1], d, nb, g0, gend, dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
