@@ -161,6 +161,37 @@ int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int
               int64_t d_in, int bits, int group_size, int sym, uint32_t* qweight,
               uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream);
 
+/* ---------------------------------------------------------------------------
+ * Two-sided adaptive rounding.  "GPTQ-2D: 三次时间复杂度的双侧自适应舍入",
+ * 方法 steps 1-3 (anti-diagonal order, entries of one anti-diagonal in
+ * parallel, errors carried through the two bases' triangular factors) and
+ * 核心洞察 (the same output as nearest-plane rounding on the vectorized,
+ * Kronecker-structured problem, in O(n^3) instead of O(n^4)).
+ *
+ * Rounds Y to the integer matrix Z, coordinate by coordinate with error
+ * feedback, under the metric || R_L (Y - Z) R_R^T ||_F^2 (scale 1, no clamp):
+ * anti-diagonals i + j = s from s = 2n-2 down to 0; for entry (i, j),
+ *   S = sum_{k>=i} R_L[i][k] P[k][j],  Z[i][j] = rint(Y[i][j] + S / (R_L[i][i] R_R[j][j])),
+ * then row i of the running array P gets (Y[i][j] - Z[i][j]) R_R[0..j][j].
+ * rint rounds half to even.  All arithmetic is float64.
+ *
+ * Y            [n x n] float64, row-major.
+ * left_basis   [n x n] float64 R_L, row-major; only the upper triangle
+ *              (diagonal included) is read.  Its diagonal must be positive.
+ * right_basis  [n x n] float64 R_R, likewise.
+ * Z            [n x n] float64 out: integer values.
+ * ws           gptq2d_workspace(n) bytes: the running array and a transposed
+ *              copy of R_R.
+ * n            1 .. GPTQ2D_MAX_N (0 is a no-op); larger n gives
+ *              GPTQ_EUNSUPPORTED.  2n-1 dependent launches are enqueued.
+ * A non-positive diagonal entry in a basis is not detected: Z is then
+ * unspecified.
+ * ------------------------------------------------------------------------- */
+#define GPTQ2D_MAX_N 32768
+int gptq2d_round(const double* Y, const double* left_basis, const double* right_basis, int64_t n,
+                 double* Z, void* ws, size_t ws_bytes, gptq_stream stream);
+size_t gptq2d_workspace(int64_t n);
+
 /* Host: static description of a status code. */
 const char* gptq_strerror(int status);
 

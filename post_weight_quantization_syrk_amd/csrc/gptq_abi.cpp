@@ -110,4 +110,19 @@ int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int
                                       qweight, scales_f16, zeros_f16, (hipStream_t)stream));
 }
 
+size_t gptq2d_workspace(int64_t n) {
+  return (n <= 0 || n > GPTQ2D_MAX_N) ? 0 : gptq::gptq2d_workspace(n);
+}
+
+int gptq2d_round(const double* Y, const double* left_basis, const double* right_basis, int64_t n,
+                 double* Z, void* ws, size_t ws_bytes, gptq_stream stream) {
+  if (n < 0) return GPTQ_EINVAL;
+  if (n > GPTQ2D_MAX_N) return GPTQ_EUNSUPPORTED;
+  if (n == 0) return GPTQ_OK;
+  if (!Y || !left_basis || !right_basis || !Z || !ws) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::gptq2d_workspace(n) || !aligned256(ws)) return GPTQ_EINVAL;
+  return hip_status(gptq::gptq2d_launch(Y, left_basis, right_basis, n, Z, ws,
+                                        (hipStream_t)stream));
+}
+
 }  // extern "C"

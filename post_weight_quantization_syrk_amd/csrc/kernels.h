@@ -40,4 +40,9 @@ hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* z
                        uint32_t* qweight, uint16_t* scales_f16, uint16_t* zeros_f16,
                        hipStream_t stream);
 
+// ---- two-sided rounding (anti-diagonal schedule) ----------------------------
+size_t gptq2d_workspace(int64_t n);
+hipError_t gptq2d_launch(const double* Y, const double* RL, const double* RR, int64_t n,
+                         double* Z, void* ws, hipStream_t stream);
+
 }  // namespace gptq

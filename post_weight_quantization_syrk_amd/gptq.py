@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         "gptq_quantize_layer": (I, [P, I, I64, I64, P, P, I, I, I, I, P, P, P, P, P, SZ, P]),
         "gptq_quantize_workspace": (SZ, [I64, I64, I]),
         "gptq_pack": (I, [P, P, P, I64, I64, I, I, I, P, P, P, P]),
+        "gptq2d_round": (I, [P, P, P, I64, P, P, SZ, P]),
+        "gptq2d_workspace": (SZ, [I64]),
         "gptq_strerror": (ctypes.c_char_p, [I]),
         "gptq_abi_version": (I, []),
     }
@@ -205,3 +207,26 @@ def gptq_pack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | N
                            int(bool(sym)), _ptr(qweight), _ptr(scales_f16), _ptr(zeros_f16),
                            _stream(stream)), "gptq_pack")
     return qweight, scales_f16, zeros_f16
+
+
+# --------------------------------------------------------------------------
+def gptq2d_workspace(n: int) -> int:
+    return int(lib().gptq2d_workspace(n))
+
+
+def gptq2d_round(Y: torch.Tensor, left_basis: torch.Tensor, right_basis: torch.Tensor,
+                 Z: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None):
+    """Two-sided rounding of Y [n, n] float64 under upper-triangular bases; returns Z (float64
+    integers).  Only the bases' upper triangles are read."""
+    n = Y.shape[0]
+    for name, t in (("Y", Y), ("left_basis", left_basis), ("right_basis", right_basis)):
+        if t.shape != (n, n) or t.dtype != torch.float64 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous float64 [n, n] tensor")
+    if Z is None:
+        Z = torch.empty((n, n), dtype=torch.float64, device=Y.device)
+    if ws is None:
+        ws = _workspace(gptq2d_workspace(n), Y.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq2d_round(_ptr(Y), _ptr(left_basis), _ptr(right_basis), n, _ptr(Z), _ptr(ws),
+                              nbytes, _stream(stream)), "gptq2d_round")
+    return Z

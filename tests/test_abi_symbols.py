@@ -82,3 +82,13 @@ def test_argument_errors_return_before_any_launch():
     # pack
     assert L.gptq_pack(fake, fake, fake, 4, 256, 5, 128, 0, fake, fake, fake, None) == gptq.GPTQ_EINVAL
     assert L.gptq_pack(fake, fake, None, 4, 256, 4, 128, 0, fake, fake, None, None) == gptq.GPTQ_EINVAL
+    # two-sided rounding: sizes, workspace, pointers
+    r = L.gptq2d_round
+    assert gptq.gptq2d_workspace(1024) == 2 * 1024 * 1024 * 8
+    assert gptq.gptq2d_workspace(0) == 0 and gptq.gptq2d_workspace(40000) == 0
+    assert r(fake, fake, fake, -1, fake, fake, 1 << 20, None) == gptq.GPTQ_EINVAL
+    assert r(fake, fake, fake, 40000, fake, fake, 1 << 40, None) == gptq.GPTQ_EUNSUPPORTED
+    assert r(fake, fake, fake, 0, fake, None, 0, None) == gptq.GPTQ_OK  # no-op
+    assert r(fake, None, fake, 16, fake, fake, 1 << 20, None) == gptq.GPTQ_EINVAL
+    assert r(fake, fake, fake, 16, fake, fake, 16, None) == gptq.GPTQ_EINVAL     # workspace too small
+    assert r(fake, fake, fake, 16, fake, P(0x1010), 1 << 20, None) == gptq.GPTQ_EINVAL  # unaligned

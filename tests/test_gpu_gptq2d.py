@@ -1,0 +1,100 @@
+"""GPU parity of the two-sided rounding path (gptq2d_round through the C ABI)
+against the float64 oracle ("GPTQ-2D: 三次时间复杂度的双侧自适应舍入", 方法 and
+关键发现: the anti-diagonal schedule gives the same integer matrix as
+nearest-plane rounding on the vectorized problem).
+
+Z is integer-valued and decided in float64 on both sides; the dot products
+are summed in a different order, so the pre-rounding values may differ in the
+last bits and a value within that distance of a half-integer could round the
+other way.  With these seeded inputs none does, and Z must match exactly."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from post_weight_quantization_syrk_amd import gptq, synth
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a ROCm GPU")
+    gptq.lib()
+
+
+def dev64(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64)).to(DEV)
+
+
+def run_gpu(Y, RL, RR, **kw) -> np.ndarray:
+    Z = gptq.gptq2d_round(dev64(Y), dev64(RL), dev64(RR), **kw)
+    torch.cuda.synchronize()
+    return Z.cpu().numpy()
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 31, 32, 64, 65, 100, 256])
+def test_gptq2d_matches_oracle(n):
+    print(f"[gptq2d] n={n}", flush=True)
+    Y, RL, RR = synth.two_sided_inputs(n)
+    Z = run_gpu(Y, RL, RR)
+    ref = oracle.two_sided_antidiagonal(Y, RL, RR)
+    np.testing.assert_array_equal(Z, ref)
+    if n <= 32:  # the quartic (vectorized) reference directly
+        np.testing.assert_array_equal(Z, oracle.two_sided_quartic(Y, RL, RR))
+
+
+def test_gptq2d_largest_size():
+    n = 1024
+    print(f"[gptq2d] n={n}", flush=True)
+    Y, RL, RR = synth.two_sided_inputs(n)
+    Z = run_gpu(Y, RL, RR)
+    ref = oracle.two_sided_antidiagonal(Y, RL, RR)
+    np.testing.assert_array_equal(Z, ref)
+    # the feedback changes the result: plain rounding differs in many entries
+    assert np.count_nonzero(Z != np.rint(Y)) > n
+
+
+def test_gptq2d_identity_bases_round_half_even():
+    n = 40
+    print(f"[gptq2d] identity n={n}", flush=True)
+    rng = np.random.default_rng(11)
+    Y = rng.standard_normal((n, n)) * 3.0
+    Y[::3, ::2] = np.round(Y[::3, ::2]) + 0.5   # exact ties: half to even
+    Z = run_gpu(Y, np.eye(n), np.eye(n))
+    np.testing.assert_array_equal(Z, np.rint(Y))
+
+
+def test_gptq2d_reads_upper_triangles_only():
+    n = 48
+    print(f"[gptq2d] lower triangles n={n}", flush=True)
+    Y, RL, RR = synth.two_sided_inputs(n)
+    rng = np.random.default_rng(5)
+    junk_l = RL + np.tril(rng.standard_normal((n, n)) * 7.0, -1)
+    junk_r = RR + np.tril(rng.standard_normal((n, n)) * 7.0, -1)
+    np.testing.assert_array_equal(run_gpu(Y, junk_l, junk_r), run_gpu(Y, RL, RR))
+
+
+def test_gptq2d_deterministic_and_workspace_reuse():
+    n_big, n_small = 200, 57
+    print(f"[gptq2d] reuse n={n_big},{n_small}", flush=True)
+    ws = torch.empty(gptq.gptq2d_workspace(n_big), dtype=torch.uint8, device=DEV)
+    Y, RL, RR = synth.two_sided_inputs(n_big)
+    a = run_gpu(Y, RL, RR, ws=ws)
+    b = run_gpu(Y, RL, RR, ws=ws)
+    np.testing.assert_array_equal(a, b)
+    Y2, RL2, RR2 = synth.two_sided_inputs(n_small)
+    c = run_gpu(Y2, RL2, RR2, ws=ws)  # smaller problem in the same (dirty) workspace
+    np.testing.assert_array_equal(c, oracle.two_sided_antidiagonal(Y2, RL2, RR2))
+
+
+def test_gptq2d_empty():
+    Z = gptq.gptq2d_round(torch.empty((0, 0), dtype=torch.float64, device=DEV),
+                          torch.empty((0, 0), dtype=torch.float64, device=DEV),
+                          torch.empty((0, 0), dtype=torch.float64, device=DEV))
+    assert Z.shape == (0, 0)
