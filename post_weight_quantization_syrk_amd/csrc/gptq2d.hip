@@ -55,7 +55,12 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
-// Anti-diagonal s: entry i_lo + 4 blockIdx.x + wave.
+constexpr int G2_B = 8;  // loads in flight per lane and operand
+
+// Anti-diagonal s: entry i_lo + 4 blockIdx.x + wave.  Loads go in batches of
+// G2_B from clamped (in-bounds) addresses, masked afterwards; the first batch
+// of the update's operands does not depend on the error and is loaded with
+// the feedback sum's.
 __global__ __launch_bounds__(256) void g2d_diag_kernel(const double* __restrict__ Y,
                                                        const double* __restrict__ RL,
                                                        const double* __restrict__ RT,
@@ -67,16 +72,54 @@ __global__ __launch_bounds__(256) void g2d_diag_kernel(const double* __restrict_
   if (i > i_hi) return;
   const int j = s - i;
   const double* rl = RL + (int64_t)i * n;
-  double acc = 0.0;
-  for (int k = i + lane; k < n; k += 64) acc = fma(rl[k], P[(int64_t)k * n + j], acc);
-  acc = wave_sum(acc);
-  const double y = Y[(int64_t)i * n + j];
   const double* rt = RT + (int64_t)j * n;
+  double* prow = P + (int64_t)i * n;
+  double pv[G2_B], tv[G2_B];
+#pragma unroll
+  for (int u = 0; u < G2_B; ++u) {
+    const int c = min(lane + 64 * u, j);
+    pv[u] = prow[c];
+    tv[u] = rt[c];
+  }
+  double acc0 = 0.0, acc1 = 0.0;
+  for (int k0 = i + lane; k0 < n + 63; k0 += 64 * G2_B) {
+    double a[G2_B], b[G2_B];
+#pragma unroll
+    for (int u = 0; u < G2_B; ++u) {
+      const int k = min(k0 + 64 * u, n - 1);
+      a[u] = rl[k];
+      b[u] = P[(int64_t)k * n + j];
+    }
+#pragma unroll
+    for (int u = 0; u < G2_B; ++u) {
+      const double x = (k0 + 64 * u < n) ? a[u] : 0.0;
+      if (u & 1) acc1 = fma(x, b[u], acc1);
+      else acc0 = fma(x, b[u], acc0);
+    }
+  }
+  const double acc = wave_sum(acc0 + acc1);
+  const double y = Y[(int64_t)i * n + j];
   const double z = rint(y + acc / (rl[i] * rt[j]));
   const double e = y - z;
   if (lane == 0) Z[(int64_t)i * n + j] = z;
-  double* prow = P + (int64_t)i * n;
-  for (int c = lane; c <= j; c += 64) prow[c] = fma(e, rt[c], prow[c]);
+#pragma unroll
+  for (int u = 0; u < G2_B; ++u) {
+    const int c = lane + 64 * u;
+    if (c <= j) prow[c] = fma(e, tv[u], pv[u]);
+  }
+  for (int c0 = lane + 64 * G2_B; c0 <= j; c0 += 64 * G2_B) {
+#pragma unroll
+    for (int u = 0; u < G2_B; ++u) {
+      const int c = min(c0 + 64 * u, j);
+      pv[u] = prow[c];
+      tv[u] = rt[c];
+    }
+#pragma unroll
+    for (int u = 0; u < G2_B; ++u) {
+      const int c = c0 + 64 * u;
+      if (c <= j) prow[c] = fma(e, tv[u], pv[u]);
+    }
+  }
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
