@@ -11,6 +11,10 @@ tokens, damping + factorization -> U, the greedy column loop with lazy
 trailing updates, and packing.  Each stage is bracketed by HIP events on the
 stream the library launches on.  Prints one JSON line on stdout; progress
 goes to stderr.
+
+--workload gptq2d instead times two-sided rounding (gptq2d_round) of an n x n
+float64 matrix under seeded upper-triangular bases triu(I + 0.1 N(0,1)),
+n = 1024 by default; one step is one whole rounding.
 """
 from __future__ import annotations
 
@@ -98,18 +102,101 @@ def cpu_baseline(wl, synth, max_seconds=30.0):
     }
 
 
+def gptq2d_bytes(n: int) -> float:
+    """Algorithmic bytes of one two-sided rounding: entry (i, j) reads R_L[i][i:]
+    and column j of the running array from row i on (16 (n - i) bytes), reads
+    and rewrites its row up to column j and reads column j of R_R (24 (j + 1)),
+    and reads Y[i][j] and writes Z[i][j] (16)."""
+    return 16.0 * n * (n * (n + 1) / 2) + 24.0 * n * (n * (n + 1) / 2) + 16.0 * n * n
+
+
+def bench_gptq2d(args):
+    import numpy as np
+    import torch
+    import oracle
+    from post_weight_quantization_syrk_amd import gptq, synth
+
+    n = args.n
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gptq.lib()
+    y, rl, rr = synth.two_sided_inputs(n)
+    Y, RL, RR = (torch.from_numpy(a).to(dev) for a in (y, rl, rr))
+    Z = torch.empty((n, n), dtype=torch.float64, device=dev)
+    ws = torch.empty(gptq.gptq2d_workspace(n), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"two-sided rounding n={n}: warmup {args.warmup}")
+    for _ in range(args.warmup):
+        gptq.gptq2d_round(Y, RL, RR, Z=Z, ws=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        gptq.gptq2d_round(Y, RL, RR, Z=Z, ws=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    launches = 2 * n - 1
+    gbs = gptq2d_bytes(n) / (ms_ev / 1e3) / 1e9
+    log(f"{ms:.3f} ms/step ({ms_ev:.3f} ms in events, {launches} anti-diagonal launches)")
+    line = {
+        "metric": f"two-sided (GPTQ-2D) rounding, matrix entries/sec/GPU (n={n})",
+        "value": round(n * n / (ms / 1e3), 1),
+        "unit": "entries/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded Y ~ N(0,1), bases triu(I + 0.1 N(0,1)))",
+        "config": {"workload": f"gptq2d_two_sided_rounding_n{n}", "n": n},
+        "roofline": {
+            "kernel": "g2d_diag_kernel (one launch per anti-diagonal)",
+            "bound": "hbm",
+            "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": round(gptq2d_bytes(n) / launches, 1),
+            "avg_launch_ms": round(ms_ev / launches, 5),
+            "note": "2n-1 dependent launches; the working set (3 n^2 float64) stays in "
+                    "the caches, so the per-launch latency, not HBM, sets the time",
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on the same problem (cpu_baseline)")
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ref = oracle.two_sided_antidiagonal(y, rl, rr)
+            dt = time.perf_counter() - t0
+        got = Z.cpu().numpy()
+        if not np.array_equal(ref, got):
+            raise RuntimeError("GPU result differs from the oracle")
+        line["cpu_baseline"] = {"value": round(n * n / dt, 1), "unit": "entries/s",
+                                "cores": 1, "kind": "oracle",
+                                "sample": f"the whole n={n} rounding ({dt:.1f} s, BLAS limited to "
+                                          "one thread)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workload", choices=["gptq", "gptq2d"], default="gptq")
+    ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the quantization path runs on a single MI355X "
               "here; run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "gptq2d":
+        bench_gptq2d(args)
+        return
 
     import torch
     from post_weight_quantization_syrk_amd import gptq, synth
