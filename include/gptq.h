@@ -162,6 +162,59 @@ int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int
               uint16_t* scales_f16, uint16_t* zeros_f16, gptq_stream stream);
 
 /* ---------------------------------------------------------------------------
+ * Activation ordering and static groups.  "GPTQ：基于近似二阶信息的大模型权重量化",
+ * GPTQ 的高级技巧: 激活排序（desc_act） (columns reordered by the summed
+ * absolute input activations, the least influential quantized first, so the
+ * error feedback lands on the more sensitive ones) and 静态与动态分组.
+ *
+ * gptq_act_order: perm[k] = the k-th column to quantize, in ascending order
+ *   of a_c = sum_t |X[t][c]| (float64), ties by column index.
+ *   X          [n_tokens x ldx] bf16 or fp32 (x_dtype), row-major, d used
+ *              columns (as for gptq_hessian_accumulate); n_tokens may be 0
+ *              (natural order).
+ *   perm       [d] int32 out.
+ *   act_sum    [d] float64 out: a_c (may be NULL).
+ *   ws         gptq_act_order_workspace(d, n_tokens) bytes.
+ *   NaN inputs leave perm unspecified.
+ *
+ * gptq_prepare_hinv_perm: gptq_prepare_hinv for the permuted matrix
+ *   H[perm][:, perm]: H is damped and mirrored in place in natural order as
+ *   before, dead[] is in natural order, U [d x d] is the upper factor of the
+ *   permuted damped matrix's inverse.  perm NULL = natural order (then
+ *   identical to gptq_prepare_hinv).  Workspace: gptq_prepare_workspace(d).
+ *
+ * gptq_quantize_layer_perm: gptq_quantize_layer with the columns processed
+ *   in the order perm (NULL = natural), U from gptq_prepare_hinv_perm with the
+ *   same perm, dead[] in natural order.  codes come back in natural column
+ *   order.  Groups:
+ *     static_groups = 0: a group is a run of group_size consecutive columns
+ *       in processing order, its parameters set at its first column from the
+ *       current (compensated) values; scales/zeros [d_out x n_groups] are
+ *       indexed by that group number.
+ *     static_groups = 1: the natural runs of group_size columns, parameters
+ *       from the original weights before any feedback; column c uses group
+ *       c / group_size.
+ *   g_idx      [d_in] int32 out (may be NULL): the group of each natural column
+ *              (dynamic: g_idx[perm[k]] = k / group_size; static: c /
+ *              group_size; group_size -1: 0).
+ *   ws         gptq_quantize_perm_workspace(d_out, d_in, block) bytes.
+ *   perm must be a permutation of 0..d-1 (d = d_in); entries outside that
+ *   range are clamped (results then unspecified, memory stays in bounds).
+ * ------------------------------------------------------------------------- */
+int gptq_act_order(const void* X, int x_dtype, int64_t n_tokens, int64_t ldx, int64_t d,
+                   int32_t* perm, double* act_sum, void* ws, size_t ws_bytes, gptq_stream stream);
+size_t gptq_act_order_workspace(int64_t d, int64_t n_tokens);
+int gptq_prepare_hinv_perm(float* H, int64_t d, double damp, const int32_t* perm, float* U,
+                           uint8_t* dead, int32_t* dev_status, void* ws, size_t ws_bytes,
+                           gptq_stream stream);
+int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                             const float* U, const uint8_t* dead, const int32_t* perm,
+                             int static_groups, int bits, int group_size, int sym, int block,
+                             uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                             float* loss_rows, void* ws, size_t ws_bytes, gptq_stream stream);
+size_t gptq_quantize_perm_workspace(int64_t d_out, int64_t d_in, int block);
+
+/* ---------------------------------------------------------------------------
  * Two-sided adaptive rounding.  "GPTQ-2D: 三次时间复杂度的双侧自适应舍入",
  * 方法 steps 1-3 (anti-diagonal order, entries of one anti-diagonal in
  * parallel, errors carried through the two bases' triangular factors) and

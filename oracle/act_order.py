@@ -72,20 +72,26 @@ def gptq_ordered(W, H0, perm, *, damp=0.01, bits=4, group_size=128, sym=False, b
         r = gptq(Wp, U, P["dead"], bits=bits, group_size=group_size, sym=sym, block=block)
         codes_p, What_p, delta_p = r["codes"], r["What"], r["delta"]
         scales, zeros = r["scales"], r["zeros"]
+        raw_q_p, raw_scales, raw_zeros = r["raw_q"], r["raw_scales"], r["raw_zeros"]
         g_idx[perm] = np.arange(d_in) // G
     else:
         maxq = maxq_for(bits)
         ng = d_in // G
         scales = np.zeros((d_out, ng))
         zeros = np.zeros((d_out, ng))
+        raw_scales = np.zeros((d_out, ng))
+        raw_zeros = np.zeros((d_out, ng))
         for g in range(ng):
-            scales[:, g], zeros[:, g] = group_params(W[:, g * G:(g + 1) * G], bits, sym)
+            scales[:, g], zeros[:, g], raw_scales[:, g], raw_zeros[:, g] = group_params(
+                W[:, g * G:(g + 1) * G], bits, sym, with_raw=True)
         codes_p = np.zeros((d_out, d_in), dtype=np.uint8)
+        raw_q_p = np.zeros((d_out, d_in))
 
         def qcol(k, Wc):
             g = perm[k] // G
             q, wh = quantize_values(Wc[:, k], scales[:, g], zeros[:, g], maxq)
             codes_p[:, k] = q.astype(np.uint8)
+            raw_q_p[:, k] = Wc[:, k] / scales[:, g]
             return wh
 
         _, What_p, delta_p = column_loop(Wp, U, qcol, block=block)
@@ -96,6 +102,9 @@ def gptq_ordered(W, H0, perm, *, damp=0.01, bits=4, group_size=128, sym=False, b
     codes[:, perm] = codes_p
     What[:, perm] = What_p
     delta[:, perm] = delta_p
+    # the *_p entries are in processing order (column k = natural column
+    # perm[k]); raw_q_p is the unrounded quotient w / scale of each code
     return dict(codes=codes, scales=scales, zeros=zeros, g_idx=g_idx, What=What, delta=delta,
                 loss_damped=np.sum(delta * delta, axis=1), U=U, dead=dead,
-                H_damped_perm=P["H"])
+                H_damped_perm=P["H"], codes_p=codes_p, What_p=What_p, raw_q_p=raw_q_p,
+                raw_scales=raw_scales, raw_zeros=raw_zeros)

@@ -110,6 +110,60 @@ int gptq_pack(const uint8_t* codes, const float* scales, const float* zeros, int
                                       qweight, scales_f16, zeros_f16, (hipStream_t)stream));
 }
 
+size_t gptq_act_order_workspace(int64_t d, int64_t n_tokens) {
+  return (d <= 0 || d > 65536 || n_tokens < 0) ? 0 : gptq::act_order_workspace(d, n_tokens);
+}
+
+int gptq_act_order(const void* X, int x_dtype, int64_t n_tokens, int64_t ldx, int64_t d,
+                   int32_t* perm, double* act_sum, void* ws, size_t ws_bytes,
+                   gptq_stream stream) {
+  if (d <= 0 || d > 65536 || n_tokens < 0 || ldx < d) return GPTQ_EINVAL;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (!perm || (n_tokens > 0 && !X)) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::act_order_workspace(d, n_tokens) || !ws || !aligned256(ws))
+    return GPTQ_EINVAL;
+  return hip_status(gptq::act_order_launch(X, x_dtype, n_tokens, ldx, d, perm, act_sum, ws,
+                                           (hipStream_t)stream));
+}
+
+int gptq_prepare_hinv_perm(float* H, int64_t d, double damp, const int32_t* perm, float* U,
+                           uint8_t* dead, int32_t* dev_status, void* ws, size_t ws_bytes,
+                           gptq_stream stream) {
+  if (d <= 0 || d > 65536 || !H || !U || !dev_status) return GPTQ_EINVAL;
+  if (!(damp >= 0.0) || !(damp < 1e30)) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::prepare_workspace(d) || !ws || !aligned256(ws)) return GPTQ_EINVAL;
+  return hip_status(gptq::prepare_perm_launch(H, d, damp, perm, U, dead, dev_status, ws,
+                                              (hipStream_t)stream));
+}
+
+size_t gptq_quantize_perm_workspace(int64_t d_out, int64_t d_in, int block) {
+  if (d_out <= 0 || d_in <= 0) return 0;
+  return gptq::quantize_perm_workspace(d_out, d_in, block);
+}
+
+int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                             const float* U, const uint8_t* dead, const int32_t* perm,
+                             int static_groups, int bits, int group_size, int sym, int block,
+                             uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                             float* loss_rows, void* ws, size_t ws_bytes, gptq_stream stream) {
+  if (d_out < 0 || d_in <= 0 || d_in > 65536) return GPTQ_EINVAL;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (bits != 2 && bits != 3 && bits != 4) return (bits == 8) ? GPTQ_EUNSUPPORTED : GPTQ_EINVAL;
+  if (!valid_group(d_in, group_size)) return GPTQ_EINVAL;
+  if (!supported_group(group_size)) return GPTQ_EUNSUPPORTED;
+  if (sym != 0 && sym != 1) return GPTQ_EINVAL;
+  if (static_groups != 0 && static_groups != 1) return GPTQ_EINVAL;
+  if (block != 128) return GPTQ_EUNSUPPORTED;
+  if (d_out == 0) return GPTQ_OK;
+  if (!W || !U || !codes || !scales || !zeros) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::quantize_perm_workspace(d_out, d_in, block) || !ws || !aligned256(ws))
+    return GPTQ_EINVAL;
+  return hip_status(gptq::quantize_perm_launch(W, w_dtype, d_out, d_in, U, dead, perm,
+                                               static_groups, bits, group_size, sym, codes,
+                                               scales, zeros, g_idx, loss_rows, ws,
+                                               (hipStream_t)stream));
+}
+
 size_t gptq2d_workspace(int64_t n) {
   return (n <= 0 || n > GPTQ2D_MAX_N) ? 0 : gptq::gptq2d_workspace(n);
 }

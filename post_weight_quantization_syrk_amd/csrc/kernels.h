@@ -26,6 +26,15 @@ hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t 
 size_t prepare_workspace(int64_t d);
 hipError_t prepare_launch(float* H, int64_t d, double damp, float* U, uint8_t* dead,
                           int32_t* dev_status, void* ws, hipStream_t stream);
+// The same for H[perm][:, perm] (perm null: natural order); dead stays in
+// natural order, U is the permuted problem's factor.
+hipError_t prepare_perm_launch(float* H, int64_t d, double damp, const int32_t* perm, float* U,
+                               uint8_t* dead, int32_t* dev_status, void* ws, hipStream_t stream);
+
+// ---- activation order: perm = columns by ascending sum_t |x_t,c| ----------
+size_t act_order_workspace(int64_t d, int64_t n_tokens);
+hipError_t act_order_launch(const void* X, int x_dtype, int64_t n_tokens, int64_t ldx, int64_t d,
+                            int32_t* perm, double* act_sum, void* ws, hipStream_t stream);
 
 // ---- quantize ------------------------------------------------------------
 size_t quantize_workspace(int64_t d_out, int64_t d_in, int block);
@@ -33,6 +42,15 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
                            const float* U, const uint8_t* dead, int bits, int group_size,
                            int sym, uint8_t* codes, float* scales, float* zeros,
                            float* loss_rows, void* ws, hipStream_t stream);
+// Columns processed in the order perm (null: natural order), static or
+// dynamic groups; codes come back in natural order, g_idx (may be null) maps
+// each column to its group.
+size_t quantize_perm_workspace(int64_t d_out, int64_t d_in, int block);
+hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                                const float* U, const uint8_t* dead, const int32_t* perm,
+                                int static_groups, int bits, int group_size, int sym,
+                                uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                                float* loss_rows, void* ws, hipStream_t stream);
 
 // ---- pack ----------------------------------------------------------------
 hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* zeros,

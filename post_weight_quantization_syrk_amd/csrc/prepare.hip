@@ -121,6 +121,25 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
   }
 }
 
+// Column order ([P1] GPTQ 的高级技巧, 激活排序): the factorization is of the
+// permuted matrix H[perm][:, perm], i.e. A[a][b] = H[perm[d-1-a]][perm[d-1-b]]
+// on A's lower triangle, gathered from H after prep_build_kernel has mirrored
+// and damped it (so the values are the ones the natural order would use).
+// perm entries are clamped to [0, d).
+__global__ __launch_bounds__(256) void prep_perm_kernel(const float* __restrict__ H, int d,
+                                                        const int32_t* __restrict__ perm,
+                                                        float* __restrict__ A) {
+  const int64_t total = (int64_t)d * d;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int a = (int)(e / d), b = (int)(e % d);
+    if (b > a) continue;
+    const int p = min(max(perm[d - 1 - a], 0), d - 1);
+    const int q = min(max(perm[d - 1 - b], 0), d - 1);
+    A[e] = H[(int64_t)p * d + q];
+  }
+}
+
 // Diagonal block: L_kk = chol(A_kk) and Dinv = L_kk^{-1}, by 256 threads in
 // four 16-column sub-steps S = [s0, s0 + 16), s0 = 16 s:
 //   A: wave 0 factors the 16 x 16 block A_SS in registers and inverts it.
@@ -747,6 +766,11 @@ size_t prepare_workspace(int64_t d) {
 
 hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t* dead,
                           int32_t* dev_status, void* ws, hipStream_t stream) {
+  return prepare_perm_launch(H, d64, damp, nullptr, U, dead, dev_status, ws, stream);
+}
+
+hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t* perm, float* U,
+                               uint8_t* dead, int32_t* dev_status, void* ws, hipStream_t stream) {
   const int d = (int)d64;
   PrepWs w = carve(ws, d64);
   hipLaunchKernelGGL(prep_stats_kernel, dim3(1), dim3(1024), 0, stream, H, d, damp, dead, w.scal,
@@ -754,6 +778,12 @@ hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t*
   const int nt32 = (int)ceil_div(d, 32);
   hipLaunchKernelGGL(prep_build_kernel, dim3(nt32 * (nt32 + 1) / 2), dim3(256), 0, stream, H, d,
                      (const double*)w.scal, w.A, w.M);
+  if (perm) {
+    const unsigned grid =
+        (unsigned)std::min<int64_t>(ceil_div((int64_t)d * d, 256), 65536);
+    hipLaunchKernelGGL(prep_perm_kernel, dim3(grid), dim3(256), 0, stream, (const float*)H, d,
+                       perm, w.A);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Steps in groups of UG: before each step of a group, its block column

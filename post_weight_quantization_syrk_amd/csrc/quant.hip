@@ -113,6 +113,60 @@ __global__ __launch_bounds__(256) void qinit_kernel(const void* __restrict__ W, 
   }
 }
 
+// Column order ([P1] GPTQ 的高级技巧, 激活排序): Wc[:, k] = W[:, perm[k]] as fp32,
+// dead columns zeroed.  perm entries are clamped to [0, d_in) (a caller that
+// passes no permutation gets garbage, never an out-of-bounds access).
+__global__ __launch_bounds__(256) void qinit_perm_kernel(const void* __restrict__ W, int w_dtype,
+                                                         int64_t d_out, int64_t d_in,
+                                                         const uint8_t* __restrict__ dead,
+                                                         const int32_t* __restrict__ perm,
+                                                         float* __restrict__ Wc) {
+  const int64_t total = d_out * d_in;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / d_in, k = e % d_in;
+    const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+    const int64_t src = r * d_in + c;
+    float v = (w_dtype == 0) ? bf16_bits_to_float(((const uint16_t*)W)[src])
+                             : ((const float*)W)[src];
+    if (dead && dead[c]) v = 0.0f;
+    Wc[e] = v;
+  }
+}
+
+// codes[:, perm[k]] = codes_p[:, k]
+__global__ __launch_bounds__(256) void unpermute_codes_kernel(const uint8_t* __restrict__ cp,
+                                                              const int32_t* __restrict__ perm,
+                                                              int64_t d_out, int64_t d_in,
+                                                              uint8_t* __restrict__ codes) {
+  const int64_t total = d_out * d_in;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / d_in, k = e % d_in;
+    const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+    codes[r * d_in + c] = cp[e];
+  }
+}
+
+// Group of each natural column: static groups c >> gshift; dynamic groups
+// follow the processing order, g_idx[perm[k]] = k >> gshift; one group per
+// row gives 0.
+__global__ __launch_bounds__(256) void gidx_kernel(const int32_t* __restrict__ perm, int64_t d_in,
+                                                   int gsize, int gshift, int static_groups,
+                                                   int32_t* __restrict__ g_idx) {
+  for (int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x; k < d_in;
+       k += (int64_t)gridDim.x * 256) {
+    if (gsize == 0) {
+      g_idx[k] = 0;
+    } else if (static_groups || !perm) {
+      g_idx[k] = (int32_t)(k >> gshift);
+    } else {
+      const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+      g_idx[c] = (int32_t)(k >> gshift);
+    }
+  }
+}
+
 struct GroupParams {
   float s, inv_s, hs, z;
   float hs_lo;  // the largest float below hs (s/2)
@@ -191,6 +245,39 @@ __global__ __launch_bounds__(256) void rowparams_kernel(const float* __restrict_
 }
 
 
+// Static groups ([P1] GPTQ 的高级技巧, 静态与动态分组): every natural group's
+// scale and zero from the original weights (dead columns zeroed), before any
+// error feedback.  One wave per (row, group); the group's columns are read
+// 64 at a time.
+__global__ __launch_bounds__(256) void static_params_kernel(const void* __restrict__ W,
+                                                            int w_dtype, int64_t d_out,
+                                                            int64_t d_in,
+                                                            const uint8_t* __restrict__ dead,
+                                                            QSpec q, float* __restrict__ scales,
+                                                            float* __restrict__ zeros) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= d_out * q.n_groups) return;
+  const int64_t row = item / q.n_groups, g = item % q.n_groups;
+  float mn = 0.0f, mx = 0.0f;  // the range always contains 0
+  for (int64_t c = g * q.gsize + lane; c < (g + 1) * q.gsize; c += 64) {
+    const int64_t e = row * d_in + c;
+    float v = (w_dtype == 0) ? bf16_bits_to_float(((const uint16_t*)W)[e]) : ((const float*)W)[e];
+    if (dead && dead[c]) v = 0.0f;
+    mn = fminf(mn, v);
+    mx = fmaxf(mx, q.sym ? fabsf(v) : v);
+  }
+  for (int m = 32; m > 0; m >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, m, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+  }
+  if (lane == 0) {
+    const GroupParams p = q.sym ? make_params(mx, 0.0f, q.maxq, 1) : make_params(mn, mx, q.maxq, 0);
+    scales[item] = p.s;
+    zeros[item] = p.z;
+  }
+}
+
 __device__ __forceinline__ float row_min(float v) {
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) v = fminf(v, __shfl_xor(v, m, 16));
@@ -202,12 +289,21 @@ __device__ __forceinline__ float row_max(float v) {
   return v;
 }
 
+// STATIC: the group parameters are given (static groups, natural groups of
+// the original weights, in scales/zeros) and column k of the block uses those
+// of group perm[b0 + k] >> gshift (perm may be null: natural order); they are
+// staged in LDS per row and column at the start.  Otherwise each group's
+// parameters are set at its first column from the current values and
+// written to scales/zeros.
+template <bool STATIC>
 __global__ __launch_bounds__(256) void colloop_kernel(
     float* __restrict__ Wc, float* __restrict__ Err, const float* __restrict__ U,
     int64_t d_out, int64_t d_in, int64_t b0, QSpec q, uint8_t* __restrict__ codes,
-    float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows) {
+    float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows,
+    const int32_t* __restrict__ perm) {
   __shared__ __attribute__((aligned(16))) float us[QB * UPITCH];
   __shared__ float invd[QB];
+  __shared__ float sps[STATIC ? 16 * QB : 1], spi[STATIC ? 16 * QB : 1], spz[STATIC ? 16 * QB : 1];
   const int tid = threadIdx.x;
   const int bw = (int)min<int64_t>(QB, d_in - b0);
   const int c = tid & 15;  // lane within the row group
@@ -239,6 +335,19 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       us[r * UPITCH + cc] = (r < bw && cc < bw) ? (cc >= r ? v[u] : 0.0f) : (r == cc ? 1.0f : 0.0f);
     }
   }
+  if constexpr (STATIC) {
+    for (int e = tid; e < 16 * QB; e += 256) {
+      const int rl = e / QB, k = e % QB;
+      const int64_t r = min<int64_t>((int64_t)blockIdx.x * 16 + rl, d_out - 1);
+      const int64_t col = b0 + min(k, bw - 1);
+      const int64_t pc = perm ? min<int64_t>(max(perm[col], 0), d_in - 1) : col;
+      const int64_t gi = r * q.n_groups + (pc >> q.gshift);
+      const float sv = scales[gi];
+      sps[e] = sv;
+      spi[e] = 1.0f / sv;
+      spz[e] = zeros[gi];
+    }
+  }
   __syncthreads();
   if (tid < QB) invd[tid] = 1.0f / us[tid * UPITCH + tid];
   __syncthreads();
@@ -264,7 +373,14 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   // LDS reads of later columns be hoisted off the dependency chain.
   StaticFor<0, QB>::run([&](auto J) {
     constexpr int j = decltype(J)::value;
-    if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
+    if constexpr (STATIC) {
+      const int e = (tid >> 4) * QB + j;
+      gp.s = sps[e];
+      gp.inv_s = spi[e];
+      gp.z = spz[e];
+      gp.hs = 0.5f * gp.s;
+      gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
+    } else if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
       if (q.gsize != 0 && (j & gmask) == 0) {
         const bool mine = (8 * c >= j) && (8 * c < j + q.gsize);
         float mn = 0.0f, mx = 0.0f;
@@ -435,17 +551,39 @@ size_t quantize_workspace(int64_t d_out, int64_t d_in, int /*block*/) {
   return 2 * align256((size_t)d_out * d_in * sizeof(float));
 }
 
+size_t quantize_perm_workspace(int64_t d_out, int64_t d_in, int block) {
+  return quantize_workspace(d_out, d_in, block) + align256((size_t)d_out * d_in);
+}
+
 hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
                            const float* U, const uint8_t* dead, int bits, int group_size, int sym,
                            uint8_t* codes, float* scales, float* zeros, float* loss_rows,
                            void* ws, hipStream_t stream) {
+  return quantize_perm_launch(W, w_dtype, d_out, d_in, U, dead, nullptr, 0, bits, group_size,
+                              sym, codes, scales, zeros, nullptr, loss_rows, ws, stream);
+}
+
+hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                                const float* U, const uint8_t* dead, const int32_t* perm,
+                                int static_groups, int bits, int group_size, int sym,
+                                uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                                float* loss_rows, void* ws, hipStream_t stream) {
   QuantWs w = carve(ws, d_out, d_in);
   const int64_t total = d_out * d_in;
-  const int vec = (d_in % 8 == 0) && ((uintptr_t)W % 16 == 0);
-  const unsigned grid =
-      (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
-  hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out, d_in,
-                     dead, w.Wc, vec);
+  // with a permutation the column loop writes codes in processing order to
+  // the workspace; they are put back in natural order at the end
+  uint8_t* codes_k = perm ? (uint8_t*)ws + quantize_workspace(d_out, d_in, QB) : codes;
+  if (perm) {
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
+    hipLaunchKernelGGL(qinit_perm_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out,
+                       d_in, dead, perm, w.Wc);
+  } else {
+    const int vec = (d_in % 8 == 0) && ((uintptr_t)W % 16 == 0);
+    const unsigned grid =
+        (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
+    hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out, d_in,
+                       dead, w.Wc, vec);
+  }
   QSpec q;
   q.maxq = (1 << bits) - 1;
   q.sym = sym ? 1 : 0;
@@ -456,6 +594,12 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
   if (q.gsize == 0)
     hipLaunchKernelGGL(rowparams_kernel, dim3((unsigned)ceil_div(d_out, 4)), dim3(256), 0, stream,
                        (const float*)w.Wc, d_out, d_in, q, scales, zeros);
+  // one group per row: static and dynamic coincide (the whole original row)
+  const bool stat = static_groups && q.gsize != 0;
+  if (stat)
+    hipLaunchKernelGGL(static_params_kernel,
+                       dim3((unsigned)ceil_div(d_out * q.n_groups, 4)), dim3(256), 0, stream, W,
+                       w_dtype, d_out, d_in, dead, q, scales, zeros);
   // Blocks in groups of QG: after each block's column loop its errors go to
   // the rest of its group only (near update, K = 128); after the group, all
   // of the group's errors go to the columns after it at once (far update,
@@ -467,8 +611,12 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
     const int64_t gcol = std::min<int64_t>(d_in, gend * QB);  // first column after the group
     for (int64_t b = g0; b < gend; ++b) {
       const int64_t b0 = b * QB;
-      hipLaunchKernelGGL(colloop_kernel, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err, U,
-                         d_out, d_in, b0, q, codes, scales, zeros, loss_rows);
+      if (stat)
+        hipLaunchKernelGGL(colloop_kernel<true>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err,
+                           U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
+      else
+        hipLaunchKernelGGL(colloop_kernel<false>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err,
+                           U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
@@ -485,6 +633,15 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (perm) {
+    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
+    hipLaunchKernelGGL(unpermute_codes_kernel, dim3(grid), dim3(256), 0, stream,
+                       (const uint8_t*)codes_k, perm, d_out, d_in, codes);
+  }
+  if (g_idx)
+    hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, 256), 1024)),
+                       dim3(256), 0, stream, perm, d_in, q.gsize, q.gshift, static_groups ? 1 : 0,
+                       g_idx);
   return hipGetLastError();
 }
 

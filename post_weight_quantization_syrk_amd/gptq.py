@@ -53,6 +53,12 @@ def lib() -> ctypes.CDLL:
         "gptq_quantize_workspace": (SZ, [I64, I64, I]),
         "gptq_pack": (I, [P, P, P, I64, I64, I, I, I, P, P, P, P]),
         "gptq2d_round": (I, [P, P, P, I64, P, P, SZ, P]),
+        "gptq_act_order": (I, [P, I, I64, I64, I64, P, P, P, SZ, P]),
+        "gptq_act_order_workspace": (SZ, [I64, I64]),
+        "gptq_prepare_hinv_perm": (I, [P, I64, D, P, P, P, P, P, SZ, P]),
+        "gptq_quantize_layer_perm": (I, [P, I, I64, I64, P, P, P, I, I, I, I, I, P, P, P, P, P,
+                                         P, SZ, P]),
+        "gptq_quantize_perm_workspace": (SZ, [I64, I64, I]),
         "gptq2d_workspace": (SZ, [I64]),
         "gptq_strerror": (ctypes.c_char_p, [I]),
         "gptq_abi_version": (I, []),
@@ -187,6 +193,97 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, dead: torch.Tensor | N
                                      _ptr(scales), _ptr(zeros), _ptr(loss_rows), _ptr(ws),
                                      nbytes, _stream(stream)), "gptq_quantize_layer")
     return codes, scales, zeros, loss_rows
+
+
+# -------------------------------------------------- activation ordering
+def gptq_act_order_workspace(d: int, n_tokens: int) -> int:
+    return int(lib().gptq_act_order_workspace(d, n_tokens))
+
+
+def gptq_act_order(X: torch.Tensor, d: int | None = None, perm=None, act_sum=None, ws=None,
+                   stream=None):
+    """perm [d] int32: columns by ascending sum_t |X[t, c]|, ties by index.
+    Returns (perm, act_sum float64 or None)."""
+    if X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a row-major [n, >=d] matrix")
+    d = X.shape[1] if d is None else d
+    n = X.shape[0]
+    if perm is None:
+        perm = torch.empty(d, dtype=torch.int32, device=X.device)
+    if ws is None:
+        ws = _workspace(gptq_act_order_workspace(d, n), X.device)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_act_order(_ptr(X), _dtype_code(X), n, X.stride(0), d, _ptr(perm),
+                                _ptr(act_sum), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_act_order")
+    return perm, act_sum
+
+
+def gptq_prepare_hinv_perm(H: torch.Tensor, perm: torch.Tensor | None, damp: float = 0.01,
+                           U=None, dead=None, status=None, ws=None, stream=None,
+                           check: bool = True):
+    """gptq_prepare_hinv for H[perm][:, perm].  Returns (U, dead, status)."""
+    d = H.shape[0]
+    dev = H.device
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != d):
+        raise ValueError("perm must be an int32 tensor of d entries")
+    if U is None:
+        U = torch.empty((d, d), dtype=torch.float32, device=dev)
+    if dead is None:
+        dead = torch.empty(d, dtype=torch.uint8, device=dev)
+    if status is None:
+        status = torch.empty(1, dtype=torch.int32, device=dev)
+    if ws is None:
+        ws = _workspace(gptq_prepare_workspace(d), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_prepare_hinv_perm(_ptr(H), d, float(damp), _ptr(perm), _ptr(U), _ptr(dead),
+                                        _ptr(status), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_prepare_hinv_perm")
+    if check:
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+        st = int(status.item())
+        if st != 0:
+            raise NotSPDError(st)
+    return U, dead, status
+
+
+def gptq_quantize_perm_workspace(d_out: int, d_in: int, block: int = 128) -> int:
+    return int(lib().gptq_quantize_perm_workspace(d_out, d_in, block))
+
+
+def gptq_quantize_layer_perm(W: torch.Tensor, U: torch.Tensor, dead: torch.Tensor | None,
+                             perm: torch.Tensor | None, *, static_groups: bool = False,
+                             bits: int = 4, group_size: int = 128, sym: bool = False,
+                             block: int = 128, codes=None, scales=None, zeros=None, g_idx=None,
+                             loss_rows=None, want_loss: bool = True, ws=None, stream=None):
+    """Returns (codes uint8 in natural column order, scales, zeros, g_idx int32, loss_rows)."""
+    d_out, d_in = W.shape
+    dev = W.device
+    if not W.is_contiguous() or not U.is_contiguous():
+        raise ValueError("W and U must be contiguous")
+    if perm is not None and (perm.dtype != torch.int32 or perm.numel() != d_in):
+        raise ValueError("perm must be an int32 tensor of d_in entries")
+    ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
+    if codes is None:
+        codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+    if scales is None:
+        scales = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+    if zeros is None:
+        zeros = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+    if g_idx is None:
+        g_idx = torch.empty(d_in, dtype=torch.int32, device=dev)
+    if loss_rows is None and want_loss:
+        loss_rows = torch.empty(d_out, dtype=torch.float32, device=dev)
+    if ws is None:
+        ws = _workspace(gptq_quantize_perm_workspace(d_out, d_in, block), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().gptq_quantize_layer_perm(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U),
+                                          _ptr(dead), _ptr(perm), int(bool(static_groups)), bits,
+                                          group_size, int(bool(sym)), block, _ptr(codes),
+                                          _ptr(scales), _ptr(zeros), _ptr(g_idx),
+                                          _ptr(loss_rows), _ptr(ws), nbytes, _stream(stream)),
+           "gptq_quantize_layer_perm")
+    return codes, scales, zeros, g_idx, loss_rows
 
 
 def gptq_pack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | None, *,

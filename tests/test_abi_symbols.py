@@ -92,3 +92,16 @@ def test_argument_errors_return_before_any_launch():
     assert r(fake, None, fake, 16, fake, fake, 1 << 20, None) == gptq.GPTQ_EINVAL
     assert r(fake, fake, fake, 16, fake, fake, 16, None) == gptq.GPTQ_EINVAL     # workspace too small
     assert r(fake, fake, fake, 16, fake, P(0x1010), 1 << 20, None) == gptq.GPTQ_EINVAL  # unaligned
+    # activation ordering, permuted factorization and quantization
+    assert L.gptq_act_order(fake, 0, 10, 8, 16, fake, None, fake, 1 << 20, None) == gptq.GPTQ_EINVAL  # ldx < d
+    assert L.gptq_act_order(fake, 0, 10, 16, 16, None, None, fake, 1 << 20, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_act_order(fake, 0, 10, 16, 16, fake, None, fake, 8, None) == gptq.GPTQ_EINVAL
+    assert L.gptq_prepare_hinv_perm(fake, 8, 0.01, None, fake, None, fake, None, 0, None) == gptq.GPTQ_EINVAL
+    qp = L.gptq_quantize_layer_perm
+    pargs = lambda static, bits=4, g=128: (fake, 0, 4, 256, fake, None, fake, static, bits, g, 0, 128,
+                                           fake, fake, fake, None, None, fake, 1 << 30, None)
+    assert qp(*pargs(2)) == gptq.GPTQ_EINVAL
+    assert qp(*pargs(0, bits=8)) == gptq.GPTQ_EUNSUPPORTED
+    assert qp(*pargs(0, g=48)) == gptq.GPTQ_EINVAL
+    assert gptq.gptq_quantize_perm_workspace(4096, 4096) == gptq.gptq_quantize_workspace(4096, 4096) + 4096 * 4096
+    assert gptq.gptq_act_order_workspace(4096, 262144) >= 256 * 4096 * 8
