@@ -56,9 +56,9 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, synth, max_seconds=30.0):
+def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=False):
     """The float64 oracle, as it stands, on a bounded sample of the workload,
-    scaled to whole-layer weights/s."""
+    scaled to whole-layer weights/s (with act_order: the ordered path)."""
     import numpy as np
     import oracle
     try:
@@ -73,20 +73,35 @@ def cpu_baseline(wl, synth, max_seconds=30.0):
     t0 = time.perf_counter()
     H0 = oracle.hessian([x])
     t_h = (time.perf_counter() - t0) * (wl.n_tokens / n_tok)
-    t0 = time.perf_counter()
-    p = oracle.prepare(H0, wl.damp)
-    t_p = time.perf_counter() - t0
     W = synth.as_f64(synth.w_matrix(wl), "bf16")[:n_rows]
-    t0 = time.perf_counter()
-    r = oracle.gptq(W, p["U"], p["dead"], bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
-                    block=wl.block)
-    t_q = (time.perf_counter() - t0) * (wl.d_out / n_rows)
+    t_a = 0.0
+    if act_order:
+        t0 = time.perf_counter()
+        perm, _ = oracle.activation_order([x])
+        t_a = (time.perf_counter() - t0) * (wl.n_tokens / n_tok)
+        Hs = np.tril(H0) + np.tril(H0, -1).T
+        t0 = time.perf_counter()
+        oracle.prepare(Hs[np.ix_(perm, perm)], wl.damp)
+        t_p = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        r = oracle.gptq_ordered(W, H0, perm, damp=wl.damp, bits=wl.bits, group_size=wl.group_size,
+                                sym=wl.sym, block=wl.block, static_groups=static_groups)
+        # gptq_ordered factorizes again: that part is not per row
+        t_q = max(0.0, time.perf_counter() - t0 - t_p) * (wl.d_out / n_rows)
+    else:
+        t0 = time.perf_counter()
+        p = oracle.prepare(H0, wl.damp)
+        t_p = time.perf_counter() - t0
+        t0 = time.perf_counter()
+        r = oracle.gptq(W, p["U"], p["dead"], bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                        block=wl.block)
+        t_q = (time.perf_counter() - t0) * (wl.d_out / n_rows)
     t0 = time.perf_counter()
     oracle.pack_rows(r["codes"], wl.bits)
     oracle.fp16_bits(r["scales"])
     oracle.fp16_bits(r["zeros"])
     t_k = (time.perf_counter() - t0) * (wl.d_out / n_rows)
-    total = t_h + t_p + t_q + t_k
+    total = t_h + t_a + t_p + t_q + t_k
     return {
         "value": wl.d_out * wl.d_in / total,
         "unit": "weights/s",
@@ -97,8 +112,8 @@ def cpu_baseline(wl, synth, max_seconds=30.0):
                    f"full 4096x4096 factorization; column loop and packing on {n_rows} of "
                    f"{wl.d_out} rows (x{wl.d_out // n_rows}); float64 numpy/LAPACK, "
                    f"elementwise numpy single-threaded"),
-        "stage_seconds_extrapolated": {"hessian": t_h, "prepare": t_p, "quantize": t_q,
-                                       "pack": t_k},
+        "stage_seconds_extrapolated": {"hessian": t_h, "act_order": t_a, "prepare": t_p,
+                                       "quantize": t_q, "pack": t_k},
     }
 
 
@@ -188,6 +203,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--workload", choices=["gptq", "gptq2d"], default="gptq")
     ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
+    ap.add_argument("--act-order", action="store_true",
+                    help="columns in activation order (gptq_act_order + the *_perm calls)")
+    ap.add_argument("--static-groups", action="store_true",
+                    help="with --act-order: static groups (parameters from the original W)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -231,22 +250,41 @@ def main():
     ws_q = torch.empty(gptq.gptq_quantize_workspace(d_out, d_in, wl.block), dtype=torch.uint8,
                        device=dev)
     stream = torch.cuda.current_stream()
-    stages = ["hessian", "prepare", "quantize", "pack"]
+    order = args.act_order
+    stages = (["hessian", "act_order", "prepare", "quantize", "pack"] if order
+              else ["hessian", "prepare", "quantize", "pack"])
+    if order:
+        perm = torch.empty(d_in, dtype=torch.int32, device=dev)
+        g_idx = torch.empty(d_in, dtype=torch.int32, device=dev)
+        ws_a = torch.empty(gptq.gptq_act_order_workspace(d_in, n), dtype=torch.uint8, device=dev)
+        ws_q = torch.empty(gptq.gptq_quantize_perm_workspace(d_out, d_in, wl.block),
+                           dtype=torch.uint8, device=dev)
 
     def step(ev=None):
+        k = 0
         H.zero_()
-        if ev: ev[0].record(stream)
+        if ev: ev[k].record(stream); k += 1
         gptq.gptq_hessian_accumulate(H, X, ws=ws_h)
-        if ev: ev[1].record(stream)
-        gptq.gptq_prepare_hinv(H, wl.damp, U, dead, status, ws=ws_p, check=False)
-        if ev: ev[2].record(stream)
-        gptq.gptq_quantize_layer(W, U, dead, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
-                                 block=wl.block, codes=codes, scales=scales, zeros=zeros,
-                                 want_loss=False, ws=ws_q)
-        if ev: ev[3].record(stream)
+        if ev: ev[k].record(stream); k += 1
+        if order:
+            gptq.gptq_act_order(X, d_in, perm=perm, ws=ws_a)
+            if ev: ev[k].record(stream); k += 1
+            gptq.gptq_prepare_hinv_perm(H, perm, wl.damp, U, dead, status, ws=ws_p, check=False)
+            if ev: ev[k].record(stream); k += 1
+            gptq.gptq_quantize_layer_perm(W, U, dead, perm, static_groups=args.static_groups,
+                                          bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                                          block=wl.block, codes=codes, scales=scales, zeros=zeros,
+                                          g_idx=g_idx, want_loss=False, ws=ws_q)
+        else:
+            gptq.gptq_prepare_hinv(H, wl.damp, U, dead, status, ws=ws_p, check=False)
+            if ev: ev[k].record(stream); k += 1
+            gptq.gptq_quantize_layer(W, U, dead, bits=wl.bits, group_size=wl.group_size,
+                                     sym=wl.sym, block=wl.block, codes=codes, scales=scales,
+                                     zeros=zeros, want_loss=False, ws=ws_q)
+        if ev: ev[k].record(stream); k += 1
         gptq.gptq_pack(codes, scales, zeros, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
                        qweight=qweight, scales_f16=s16, zeros_f16=z16)
-        if ev: ev[4].record(stream)
+        if ev: ev[k].record(stream); k += 1
 
     log(f"warmup {args.warmup} steps")
     for _ in range(args.warmup):
@@ -255,7 +293,8 @@ def main():
     if int(status.item()) != 0:
         raise RuntimeError("factorization failed during warmup")
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(args.steps)]
     log(f"timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -302,7 +341,8 @@ def main():
         "data": "synthetic (seeded; stands in for a 7B model's weights and 128x2048 calibration tokens)",
         "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "tokens": n,
                    "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym,
-                   "block": wl.block, "damp": wl.damp},
+                   "block": wl.block, "damp": wl.damp, "act_order": bool(order),
+                   "static_groups": bool(order and args.static_groups)},
         "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "secondary": {"metric": "SYRK+update TFLOP/s", "value": round(upd_tflops, 2),
                       "unit": "TFLOP/s",
@@ -312,7 +352,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample (cpu_baseline)")
-        line["cpu_baseline"] = cpu_baseline(wl, synth)
+        line["cpu_baseline"] = cpu_baseline(wl, synth, act_order=order,
+                                            static_groups=bool(order and args.static_groups))
     print(json.dumps(line), flush=True)
 
 

@@ -129,14 +129,16 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
 __global__ __launch_bounds__(256) void prep_perm_kernel(const float* __restrict__ H, int d,
                                                         const int32_t* __restrict__ perm,
                                                         float* __restrict__ A) {
-  const int64_t total = (int64_t)d * d;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * 256) {
-    const int a = (int)(e / d), b = (int)(e % d);
-    if (b > a) continue;
+  // grid: x over columns b, y over rows a (strided)
+  const int b = (int)blockIdx.x * 256 + (int)threadIdx.x;
+  if (b >= d) return;
+  const int q = min(max(perm[d - 1 - b], 0), d - 1);
+  const int G = (int)gridDim.y;
+  int a0 = (int)blockIdx.y;  // rows a0, a0 + G, ...: the first one >= b
+  if (a0 < b) a0 += ((b - a0 + G - 1) / G) * G;
+  for (int a = a0; a < d; a += G) {
     const int p = min(max(perm[d - 1 - a], 0), d - 1);
-    const int q = min(max(perm[d - 1 - b], 0), d - 1);
-    A[e] = H[(int64_t)p * d + q];
+    A[(int64_t)a * d + b] = H[(int64_t)p * d + q];
   }
 }
 
@@ -778,12 +780,10 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
   const int nt32 = (int)ceil_div(d, 32);
   hipLaunchKernelGGL(prep_build_kernel, dim3(nt32 * (nt32 + 1) / 2), dim3(256), 0, stream, H, d,
                      (const double*)w.scal, w.A, w.M);
-  if (perm) {
-    const unsigned grid =
-        (unsigned)std::min<int64_t>(ceil_div((int64_t)d * d, 256), 65536);
-    hipLaunchKernelGGL(prep_perm_kernel, dim3(grid), dim3(256), 0, stream, (const float*)H, d,
-                       perm, w.A);
-  }
+  if (perm)
+    hipLaunchKernelGGL(prep_perm_kernel,
+                       dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 1024)), dim3(256), 0,
+                       stream, (const float*)H, d, perm, w.A);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Steps in groups of UG: before each step of a group, its block column

@@ -121,16 +121,16 @@ __global__ __launch_bounds__(256) void qinit_perm_kernel(const void* __restrict_
                                                          const uint8_t* __restrict__ dead,
                                                          const int32_t* __restrict__ perm,
                                                          float* __restrict__ Wc) {
-  const int64_t total = d_out * d_in;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t r = e / d_in, k = e % d_in;
-    const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+  // grid: x over columns, y over rows (strided)
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= d_in) return;
+  const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+  const bool dc = dead && dead[c];
+  for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y) {
     const int64_t src = r * d_in + c;
-    float v = (w_dtype == 0) ? bf16_bits_to_float(((const uint16_t*)W)[src])
-                             : ((const float*)W)[src];
-    if (dead && dead[c]) v = 0.0f;
-    Wc[e] = v;
+    const float v = (w_dtype == 0) ? bf16_bits_to_float(((const uint16_t*)W)[src])
+                                   : ((const float*)W)[src];
+    Wc[r * d_in + k] = dc ? 0.0f : v;
   }
 }
 
@@ -139,13 +139,10 @@ __global__ __launch_bounds__(256) void unpermute_codes_kernel(const uint8_t* __r
                                                               const int32_t* __restrict__ perm,
                                                               int64_t d_out, int64_t d_in,
                                                               uint8_t* __restrict__ codes) {
-  const int64_t total = d_out * d_in;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * 256) {
-    const int64_t r = e / d_in, k = e % d_in;
-    const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
-    codes[r * d_in + c] = cp[e];
-  }
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (k >= d_in) return;
+  const int64_t c = min<int64_t>(max(perm[k], 0), d_in - 1);
+  for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y) codes[r * d_in + c] = cp[r * d_in + k];
 }
 
 // Group of each natural column: static groups c >> gshift; dynamic groups
@@ -573,10 +570,10 @@ hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64
   // with a permutation the column loop writes codes in processing order to
   // the workspace; they are put back in natural order at the end
   uint8_t* codes_k = perm ? (uint8_t*)ws + quantize_workspace(d_out, d_in, QB) : codes;
+  const dim3 pgrid((unsigned)ceil_div(d_in, 256), (unsigned)std::min<int64_t>(d_out, 1024));
   if (perm) {
-    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
-    hipLaunchKernelGGL(qinit_perm_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out,
-                       d_in, dead, perm, w.Wc);
+    hipLaunchKernelGGL(qinit_perm_kernel, pgrid, dim3(256), 0, stream, W, w_dtype, d_out, d_in,
+                       dead, perm, w.Wc);
   } else {
     const int vec = (d_in % 8 == 0) && ((uintptr_t)W % 16 == 0);
     const unsigned grid =
@@ -633,11 +630,9 @@ hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (perm) {
-    const unsigned grid = (unsigned)std::min<int64_t>(ceil_div(total, 256), 65536);
-    hipLaunchKernelGGL(unpermute_codes_kernel, dim3(grid), dim3(256), 0, stream,
+  if (perm)
+    hipLaunchKernelGGL(unpermute_codes_kernel, pgrid, dim3(256), 0, stream,
                        (const uint8_t*)codes_k, perm, d_out, d_in, codes);
-  }
   if (g_idx)
     hipLaunchKernelGGL(gidx_kernel, dim3((unsigned)std::min<int64_t>(ceil_div(d_in, 256), 1024)),
                        dim3(256), 0, stream, perm, d_in, q.gsize, q.gshift, static_groups ? 1 : 0,
