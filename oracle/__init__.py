@@ -21,11 +21,13 @@ from .storage import (bits_per_weight, model_gigabytes, round_half_up, pack_rows
                       unpack_rows, words_per_row, fp16_bits)
 from .gptq2d_oracle import two_sided_quartic, two_sided_antidiagonal
 from .act_order import activation_order, gptq_ordered
+from .dequant_gemm import dequantize, dequant_matmul
 
 __all__ = [
     "NotSPD", "hessian", "hessian_entry", "prepare", "reversed_route_U", "group_params",
     "quantize_values", "gptq", "column_loop", "rtn", "layer_loss", "fp16_rne",
     "maxq_for", "bits_per_weight", "model_gigabytes", "round_half_up", "pack_rows",
     "unpack_rows", "words_per_row", "fp16_bits", "two_sided_quartic",
-    "two_sided_antidiagonal", "activation_order", "gptq_ordered",
+    "two_sided_antidiagonal", "activation_order", "gptq_ordered", "dequantize",
+    "dequant_matmul",
 ]
