@@ -215,6 +215,32 @@ int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t 
 size_t gptq_quantize_perm_workspace(int64_t d_out, int64_t d_in, int block);
 
 /* ---------------------------------------------------------------------------
+ * Dequantized product with the packed 4-bit weights (W4A16).
+ * "GPTQ：基于近似二阶信息的大模型权重量化", 阶段三 (inference on the integer codes
+ * with their group scale and zero) and "GPTQ/AWQ量化中Group Size的精确含义与计算",
+ * 存储代价 (a 16-bit scale and a zero per group of g columns).
+ *
+ *   Y[i][n] = sum_k X[i][k] W_hat[n][k],
+ *   W_hat[n][k] = s[n][k/g] (q[n][k] - z[n][k/g])   (g = d_in when group_size = -1)
+ *
+ * X           [m x ldx] bf16, row-major, d_in used columns; 16-byte aligned,
+ *             ldx a multiple of 8.
+ * qweight     [d_out x d_in/8] uint32: gptq_pack's 4-bit layout (code k of a
+ *             row in bits 4(k%8) .. 4(k%8)+3 of word k/8).
+ * scales_f16, zeros_f16  [d_out x n_groups] binary16 bits as gptq_pack writes
+ *             them; with sym = 1 zeros_f16 is not read and z = 8.
+ * Y           [m x d_out] float32 out.
+ * d_in must be a multiple of 128 (GPTQ_EUNSUPPORTED otherwise); group_size
+ * 32, 64, 128 or -1.  Groups are the natural runs of g columns (the plain
+ * path, or static groups with activation ordering).  Every product
+ * x (q - z) is exact in fp32; each group's sum is scaled by s in fp32, so
+ * only fp32 accumulation rounds.
+ * ------------------------------------------------------------------------- */
+int gptq_w4a16_matmul(const void* X, int64_t m, int64_t ldx, const uint32_t* qweight,
+                      const uint16_t* scales_f16, const uint16_t* zeros_f16, int64_t d_out,
+                      int64_t d_in, int group_size, int sym, float* Y, gptq_stream stream);
+
+/* ---------------------------------------------------------------------------
  * Two-sided adaptive rounding.  "GPTQ-2D: 三次时间复杂度的双侧自适应舍入",
  * 方法 steps 1-3 (anti-diagonal order, entries of one anti-diagonal in
  * parallel, errors carried through the two bases' triangular factors) and

@@ -15,7 +15,7 @@ LIB_NAME = "libgptq_mi355x.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 
 SOURCES = ["syrk.hip", "prepare.hip", "quant.hip", "gptq2d.hip", "act_order.hip",
-           "gptq_abi.cpp"]
+           "w4a16.hip", "gptq_abi.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -164,6 +164,22 @@ int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t 
                                                (hipStream_t)stream));
 }
 
+int gptq_w4a16_matmul(const void* X, int64_t m, int64_t ldx, const uint32_t* qweight,
+                      const uint16_t* scales_f16, const uint16_t* zeros_f16, int64_t d_out,
+                      int64_t d_in, int group_size, int sym, float* Y, gptq_stream stream) {
+  if (m < 0 || d_out <= 0 || d_in <= 0 || d_in > 65536 || d_out > (1 << 30)) return GPTQ_EINVAL;
+  if (!valid_group(d_in, group_size)) return GPTQ_EINVAL;
+  if (!supported_group(group_size)) return GPTQ_EUNSUPPORTED;
+  if (sym != 0 && sym != 1) return GPTQ_EINVAL;
+  if (d_in % 128 != 0) return GPTQ_EUNSUPPORTED;
+  if (m == 0) return GPTQ_OK;
+  if (m > (1 << 30) || ldx < d_in || ldx % 8 != 0) return GPTQ_EINVAL;
+  if (!X || !qweight || !scales_f16 || !Y || (!sym && !zeros_f16)) return GPTQ_EINVAL;
+  if ((uintptr_t)X % 16 != 0) return GPTQ_EINVAL;
+  return hip_status(gptq::w4a16_launch(X, m, ldx, qweight, scales_f16, sym ? nullptr : zeros_f16,
+                                       d_out, d_in, group_size, Y, (hipStream_t)stream));
+}
+
 size_t gptq2d_workspace(int64_t n) {
   return (n <= 0 || n > GPTQ2D_MAX_N) ? 0 : gptq::gptq2d_workspace(n);
 }

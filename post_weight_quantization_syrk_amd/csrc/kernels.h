@@ -58,6 +58,11 @@ hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* z
                        uint32_t* qweight, uint16_t* scales_f16, uint16_t* zeros_f16,
                        hipStream_t stream);
 
+// ---- dequantized product with 4-bit packed weights ------------------------
+hipError_t w4a16_launch(const void* X, int64_t m, int64_t ldx, const uint32_t* qweight,
+                        const uint16_t* scales_f16, const uint16_t* zeros_f16, int64_t d_out,
+                        int64_t d_in, int group_size, float* Y, hipStream_t stream);
+
 // ---- two-sided rounding (anti-diagonal schedule) ----------------------------
 size_t gptq2d_workspace(int64_t n);
 hipError_t gptq2d_launch(const double* Y, const double* RL, const double* RR, int64_t n,

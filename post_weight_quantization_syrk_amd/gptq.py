@@ -53,6 +53,7 @@ def lib() -> ctypes.CDLL:
         "gptq_quantize_workspace": (SZ, [I64, I64, I]),
         "gptq_pack": (I, [P, P, P, I64, I64, I, I, I, P, P, P, P]),
         "gptq2d_round": (I, [P, P, P, I64, P, P, SZ, P]),
+        "gptq_w4a16_matmul": (I, [P, I64, I64, P, P, P, I64, I64, I, I, P, P]),
         "gptq_act_order": (I, [P, I, I64, I64, I64, P, P, P, SZ, P]),
         "gptq_act_order_workspace": (SZ, [I64, I64]),
         "gptq_prepare_hinv_perm": (I, [P, I64, D, P, P, P, P, P, SZ, P]),
@@ -327,3 +328,21 @@ def gptq2d_round(Y: torch.Tensor, left_basis: torch.Tensor, right_basis: torch.T
     _check(lib().gptq2d_round(_ptr(Y), _ptr(left_basis), _ptr(right_basis), n, _ptr(Z), _ptr(ws),
                               nbytes, _stream(stream)), "gptq2d_round")
     return Z
+
+
+# --------------------------------------------------------------------------
+def gptq_w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales_f16: torch.Tensor,
+                      zeros_f16: torch.Tensor | None, *, group_size: int, sym: bool,
+                      Y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Y [m, d_out] fp32 = X [m, d_in] bf16 times the dequantized 4-bit weights (gptq_pack's
+    qweight, scales_f16, zeros_f16) transposed."""
+    if X.dtype != torch.bfloat16 or X.dim() != 2 or X.stride(1) != 1:
+        raise ValueError("X must be a row-major bf16 [m, d_in] matrix")
+    m, d_in = X.shape
+    d_out = qweight.shape[0]
+    if Y is None:
+        Y = torch.empty((m, d_out), dtype=torch.float32, device=X.device)
+    _check(lib().gptq_w4a16_matmul(_ptr(X), m, X.stride(0), _ptr(qweight), _ptr(scales_f16),
+                                   _ptr(zeros_f16), d_out, d_in, group_size, int(bool(sym)),
+                                   _ptr(Y), _stream(stream)), "gptq_w4a16_matmul")
+    return Y

@@ -105,3 +105,12 @@ def test_argument_errors_return_before_any_launch():
     assert qp(*pargs(0, g=48)) == gptq.GPTQ_EINVAL
     assert gptq.gptq_quantize_perm_workspace(4096, 4096) == gptq.gptq_quantize_workspace(4096, 4096) + 4096 * 4096
     assert gptq.gptq_act_order_workspace(4096, 262144) >= 256 * 4096 * 8
+    # dequantized product
+    w = L.gptq_w4a16_matmul
+    assert w(fake, 4, 256, fake, fake, fake, 8, 200, 128, 0, fake, None) == gptq.GPTQ_EINVAL      # 128 does not divide 200
+    assert w(fake, 4, 192, fake, fake, fake, 8, 192, 64, 0, fake, None) == gptq.GPTQ_EUNSUPPORTED  # d_in % 128
+    assert w(fake, 4, 250, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL      # ldx < d_in
+    assert w(fake, 4, 260, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL      # ldx % 8
+    assert w(fake, 4, 256, fake, fake, None, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL      # zeros needed
+    assert w(P(0x1008), 4, 256, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL  # unaligned X
+    assert w(fake, 0, 256, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_OK         # no rows
