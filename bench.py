@@ -14,7 +14,9 @@ goes to stderr.
 
 --workload gptq2d instead times two-sided rounding (gptq2d_round) of an n x n
 float64 matrix under seeded upper-triangular bases triu(I + 0.1 N(0,1)),
-n = 1024 by default; one step is one whole rounding.
+n = 1024 by default; one step is one whole rounding.  --workload w4a16 times
+the dequantized 4-bit product (gptq_w4a16_matmul) of an m x 4096 bf16 X with
+the packed 4096 x 4096 g128 weights (m = 4096 by default).
 """
 from __future__ import annotations
 
@@ -195,13 +197,87 @@ def bench_gptq2d(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_w4a16(args):
+    """Y = X W_hat^T with the packed 4-bit weights of the attention projection
+    (4096 x 4096, g128 asymmetric), X m x 4096 bf16."""
+    import numpy as np
+    import torch
+    import oracle
+    from post_weight_quantization_syrk_amd import gptq, synth
+
+    m, d_in, d_out, g = args.m, 4096, 4096, 128
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gptq.lib()
+    rng = np.random.default_rng(7)
+    codes = rng.integers(0, 16, size=(d_out, d_in), dtype=np.uint8)
+    scales = oracle.fp16_rne(np.exp(rng.uniform(-6.0, -2.0, size=(d_out, d_in // g))))
+    zeros = rng.integers(0, 16, size=(d_out, d_in // g)).astype(np.float64)
+    qw = oracle.pack_rows(codes, 4)
+    s16, z16 = oracle.fp16_bits(scales), oracle.fp16_bits(zeros)
+    xb = synth.f32_to_bf16_bits(rng.standard_normal((m, d_in), dtype=np.float32))
+    X = torch.from_numpy(xb.view(np.int16)).to(dev).view(torch.bfloat16)
+    Q = torch.from_numpy(qw.astype(np.uint32).view(np.int32)).to(dev)
+    S = torch.from_numpy(s16.view(np.int16)).to(dev)
+    Z = torch.from_numpy(z16.view(np.int16)).to(dev)
+    Y = torch.empty((m, d_out), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        gptq.gptq_w4a16_matmul(X, Q, S, Z, group_size=g, sym=False, Y=Y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        gptq.gptq_w4a16_matmul(X, Q, S, Z, group_size=g, sym=False, Y=Y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_ev = e0.elapsed_time(e1) / args.steps
+    flops = 2.0 * m * d_in * d_out
+    tf = flops / (ms_ev / 1e3) / 1e12
+    log(f"w4a16 m={m}: {ms:.4f} ms/call ({ms_ev:.4f} ms in events), {tf:.1f} TFLOP/s")
+    line = {
+        "metric": f"W4A16 dequantized product, output elements/sec/GPU (m={m}, 4096x4096 g128)",
+        "value": round(m * d_out / (ms / 1e3), 1),
+        "unit": "elements/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded codes, binary16 scales and zeros, X ~ N(0,1) bf16)",
+        "config": {"workload": f"w4a16_m{m}_4096x4096_g128", "m": m, "d_in": d_in,
+                   "d_out": d_out, "group_size": g},
+        "roofline": {
+            "kernel": "w4a16_kernel", "bound": "mfma", "achieved": round(tf, 2),
+            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None, "algorithmic_flops_per_launch": flops,
+            "avg_launch_ms": round(ms_ev, 5),
+        },
+    }
+    if not args.no_cpu_baseline:
+        rows = min(m, 256)
+        x64 = synth.as_f64(xb[:rows], "bf16")
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        t0 = time.perf_counter()
+        oracle.dequant_matmul(x64, qw, s16, z16, bits=4, group_size=g, sym=False)
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(rows * d_out / dt, 1), "unit": "elements/s",
+                                "cores": cores, "kind": "oracle",
+                                "sample": f"{rows} of {m} rows of X, the whole weight "
+                                          f"dequantized ({dt:.2f} s)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["gptq", "gptq2d"], default="gptq")
+    ap.add_argument("--workload", choices=["gptq", "gptq2d", "w4a16"], default="gptq")
+    ap.add_argument("--m", type=int, default=4096, help="rows of X for --workload w4a16")
     ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
     ap.add_argument("--act-order", action="store_true",
                     help="columns in activation order (gptq_act_order + the *_perm calls)")
@@ -215,6 +291,9 @@ def main():
         sys.exit(2)
     if args.workload == "gptq2d":
         bench_gptq2d(args)
+        return
+    if args.workload == "w4a16":
+        bench_w4a16(args)
         return
 
     import torch

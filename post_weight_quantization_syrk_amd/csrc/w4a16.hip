@@ -15,8 +15,14 @@
 //
 // Tile: 128 (M) x 128 (N) per workgroup; wave w owns columns 32 w .. 32 w + 31
 // of it and all 128 rows, as four 32 x 32 blocks, so each dequantized word
-// feeds four MFMAs.  K runs in chunks of 4 steps of 16, the next chunk's
-// operands loaded while the current one multiplies.
+// feeds four MFMAs.  K runs in chunks of 64: the chunk's X tile (128 rows x
+// 128 bytes) and packed words (128 rows x 32 bytes) are loaded with coalesced
+// 16-byte loads into double-buffered LDS (the next chunk's loads in flight
+// while the current one multiplies; one barrier per chunk).  Within a chunk,
+// MFMA kk and lane half h take k = 32 (kk / 2) + 16 h + 8 (kk % 2) + 0..7, so
+// each MFMA stays inside a group of 32 and a lane's two words for MFMAs 2j,
+// 2j + 1 are adjacent (one 8-byte LDS read).  Row pitches of 144 bytes (X)
+// and 40 bytes (words) keep the LDS reads free of bank conflicts.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +34,6 @@ namespace gptq {
 namespace {
 
 constexpr int WA_M = 128, WA_N = 128;
-constexpr int WA_KC = 4;  // k-steps (of 16) per chunk
 
 __device__ __forceinline__ float f16_bits_to_float(uint16_t b) {
   return __half2float(__ushort_as_half(b));
@@ -48,22 +53,54 @@ __device__ __forceinline__ bf16x8 dequant_word(uint32_t w, float z) {
   return r;
 }
 
+constexpr int WA_KCH = 64;         // k per chunk
+constexpr int XP = WA_KCH + 8;     // X tile pitch (bf16 elements): 144 bytes
+constexpr int WP = 10;             // word tile pitch (uint32): 8 words + 2
+
 __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__ X, int64_t ldx,
                                                     int M, int N, int K,
                                                     const uint32_t* __restrict__ Q,
                                                     const uint16_t* __restrict__ S16,
                                                     const uint16_t* __restrict__ Z16, int G,
                                                     float* __restrict__ Y) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][WA_M * XP];
+  __shared__ __attribute__((aligned(16))) uint32_t ws[2][WA_N * WP];
+  __shared__ float psz[2][WA_N][2][2];  // per column: (scale, zero) of the chunk's groups
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
-  const int m0 = blockIdx.y * WA_M, n0 = blockIdx.x * WA_N + 32 * wave;
-  const int wpr = K / 8, ng = K / G, gsteps = G / 16, nsteps = K / 16;
-  const int n = min(n0 + l32, N - 1);
-  const uint32_t* qrow = Q + (int64_t)n * wpr + h;
-  const uint16_t* xrow[4];
+  const int m0 = blockIdx.y * WA_M, nb = blockIdx.x * WA_N, n0 = nb + 32 * wave;
+  const int wpr = K / 8, ng = K / G, nch = K / WA_KCH;
+  // global -> LDS: X rows tid/8 + 32 i (16 bytes at 8 (tid % 8)), word rows
+  // tid/2 (16 bytes at 4 (tid % 2))
+  const uint16_t* xg[4];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-    xrow[mi] = X + (int64_t)min(m0 + 32 * mi + l32, M - 1) * ldx + 8 * h;
+  for (int i = 0; i < 4; ++i)
+    xg[i] = X + (int64_t)min(m0 + (tid >> 3) + 32 * i, M - 1) * ldx + 8 * (tid & 7);
+  const uint32_t* qg = Q + (int64_t)min(nb + (tid >> 1), N - 1) * wpr + 4 * (tid & 1);
+  // group parameters: thread t stages column t/2, slot t%2 (the chunk's first
+  // group and the next; one group per chunk unless g = 32)
+  const int pcol = min(nb + (tid >> 1), N - 1), pslot = tid & 1;
+  uint4 xr[4], qr;
+  uint16_t sr, zr;
+  auto gload = [&](int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xr[i] = *(const uint4*)(xg[i] + (int64_t)c * WA_KCH);
+    qr = *(const uint4*)(qg + (int64_t)c * (WA_KCH / 8));
+    const int g = min(c * WA_KCH / G + pslot, ng - 1);
+    sr = S16[(int64_t)pcol * ng + g];
+    zr = Z16 ? Z16[(int64_t)pcol * ng + g] : (uint16_t)0;
+  };
+  auto lstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *(uint4*)(&xs[buf][((tid >> 3) + 32 * i) * XP + 8 * (tid & 7)]) = xr[i];
+    // 8-byte stores: rows are 40 bytes apart, so 8-byte aligned
+    uint2* wdst = (uint2*)(&ws[buf][(tid >> 1) * WP + 4 * (tid & 1)]);
+    wdst[0] = make_uint2(qr.x, qr.y);
+    wdst[1] = make_uint2(qr.z, qr.w);
+    psz[buf][tid >> 1][pslot][0] = f16_bits_to_float(sr);
+    psz[buf][tid >> 1][pslot][1] = Z16 ? f16_bits_to_float(zr) : 8.0f;  // sym 4-bit: 8
+  };
   f32x16 tot[4], acc[4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
@@ -72,46 +109,32 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
       tot[mi][i] = 0.0f;
       acc[mi][i] = 0.0f;
     }
-  struct Ops {
-    bf16x8 a[WA_KC][4];
-    uint32_t b[WA_KC];
-  };
-  auto load = [&](Ops& o, int ks) __attribute__((always_inline)) {
+  float s = 0.0f, z = 8.0f;
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) gload(c + 1);
+    const uint16_t* xb = xs[buf];
+    const uint32_t* wb = ws[buf] + (32 * wave + l32) * WP + 2 * h;
 #pragma unroll
-    for (int kk = 0; kk < WA_KC; ++kk) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) o.a[kk][mi] = *(const bf16x8*)(xrow[mi] + 16 * (ks + kk));
-      o.b[kk] = qrow[2 * (ks + kk)];
-    }
-  };
-  // the lane's column's scale and zero, one group ahead
-  const uint16_t* srow = S16 + (int64_t)n * ng;
-  const uint16_t* zrow = Z16 ? Z16 + (int64_t)n * ng : nullptr;
-  uint16_t s_b = srow[0], z_b = zrow ? zrow[0] : 0;
-  uint16_t s_nb = srow[min(1, ng - 1)], z_nb = zrow ? zrow[min(1, ng - 1)] : 0;
-  float s = 0.0f, z = 8.0f;  // symmetric 4-bit: z = (maxq + 1) / 2
-  // one chunk: multiply c (steps ks ..), having started the loads of the
-  // next chunk into nx
-  auto chunk = [&](Ops& c, Ops& nx, int ks) __attribute__((always_inline)) {
-    if (ks + WA_KC < nsteps) load(nx, ks + WA_KC);
-#pragma unroll
-    for (int kk = 0; kk < WA_KC; ++kk) {
-      const int step = ks + kk;
-      if (step % gsteps == 0) {  // a group starts: take its parameters, fetch a later one's
-        const int g = step / gsteps;
-        s = f16_bits_to_float(s_b);
-        if (zrow) z = f16_bits_to_float(z_b);
-        s_b = s_nb;
-        z_b = z_nb;
-        const int gn = min(g + 2, ng - 1);
-        s_nb = srow[gn];
-        if (zrow) z_nb = zrow[gn];
+    for (int kk = 0; kk < 4; ++kk) {
+      const int k0 = c * WA_KCH + 32 * (kk >> 1) + 16 * (kk & 1);  // first k of this MFMA
+      if (k0 % G == 0) {  // a group starts: its parameters, staged with the chunk
+        const int slot = (k0 - c * WA_KCH) / G;
+        s = psz[buf][32 * wave + l32][slot][0];
+        z = psz[buf][32 * wave + l32][slot][1];
       }
-      const bf16x8 bv = dequant_word(c.b[kk], z);
+      const uint32_t word = wb[4 * (kk >> 1) + (kk & 1)];
+      const bf16x8 bv = dequant_word(word, z);
+      const int koff = 32 * (kk >> 1) + 16 * h + 8 * (kk & 1);
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(c.a[kk][mi], bv, acc[mi], 0, 0, 0);
-      if ((step + 1) % gsteps == 0) {  // the group ends: scale it into the total
+      for (int mi = 0; mi < 4; ++mi) {
+        const bf16x8 av = *(const bf16x8*)(xb + (32 * mi + l32) * XP + koff);
+        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[mi], 0, 0, 0);
+      }
+      if ((k0 + 16) % G == 0) {  // the group ends: scale it into the total
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
@@ -121,12 +144,16 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
           }
       }
     }
-  };
-  Ops o0, o1;
-  load(o0, 0);
-  for (int ks = 0; ks < nsteps; ks += 2 * WA_KC) {
-    chunk(o0, o1, ks);
-    if (ks + WA_KC < nsteps) chunk(o1, o0, ks + WA_KC);
+    if (c + 1 < nch) {
+      // keep the stores of the next chunk after this chunk's products, so its
+      // loads have the whole chunk to arrive
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        asm volatile("" : "+v"(xr[i].x), "+v"(xr[i].y), "+v"(xr[i].z), "+v"(xr[i].w));
+      asm volatile("" : "+v"(qr.x), "+v"(qr.y), "+v"(qr.z), "+v"(qr.w));
+      lstore(buf ^ 1);
+    }
+    __syncthreads();
   }
   const int col = n0 + l32;
   if (col >= N) return;
