@@ -58,7 +58,7 @@ def traffic_from_profile():
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=False):
+def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=False, n_mats=1):
     """The float64 oracle, as it stands, on a bounded sample of the workload,
     scaled to whole-layer weights/s (with act_order: the ordered path)."""
     import numpy as np
@@ -103,9 +103,10 @@ def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=Fal
     oracle.fp16_bits(r["scales"])
     oracle.fp16_bits(r["zeros"])
     t_k = (time.perf_counter() - t0) * (wl.d_out / n_rows)
-    total = t_h + t_a + t_p + t_q + t_k
+    # n_mats matrices share the Hessian and the factorization
+    total = t_h + t_a + t_p + n_mats * (t_q + t_k)
     return {
-        "value": wl.d_out * wl.d_in / total,
+        "value": n_mats * wl.d_out * wl.d_in / total,
         "unit": "weights/s",
         "cores": cores,
         "blas_threads": blas_threads,
@@ -270,13 +271,122 @@ def bench_w4a16(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_shared(args):
+    """The feed-forward gate and up projections (11008 x 4096 each, bf16) from one
+    Hessian of 131072 tokens, 3-bit symmetric g64: one step = zero H, H += 2 X^T X,
+    prepare, gptq_quantize_layers on both matrices, pack."""
+    import torch
+    from post_weight_quantization_syrk_amd import gptq, synth
+
+    wl = synth.FFN_GATE
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    gptq.lib()
+    d_out, d_in, n = wl.d_out, wl.d_in, wl.n_tokens
+    log(f"generating inputs: X {n}x{d_in} bf16, gate and up {d_out}x{d_in} bf16")
+    xb = synth.x_full(wl)
+    X = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+    del xb
+    Ws = [torch.from_numpy(synth.w_matrix(wl, tensor=t).view("int16")).to(dev).view(torch.bfloat16)
+          for t in (0, 7)]
+    H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
+    U = torch.empty((d_in, d_in), dtype=torch.float32, device=dev)
+    dead = torch.empty(d_in, dtype=torch.uint8, device=dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+    rows = 2 * d_out
+    ng = d_in // wl.group_size
+    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, gptq.GPTQ_BF16), dtype=torch.uint8,
+                       device=dev)
+    ws_p = torch.empty(gptq.gptq_prepare_workspace(d_in), dtype=torch.uint8, device=dev)
+    ws_q = torch.empty(gptq.gptq_quantize_workspace(rows, d_in, wl.block), dtype=torch.uint8,
+                       device=dev)
+    qweight = torch.empty((rows, d_in * wl.bits // 32), dtype=torch.int32, device=dev)
+    s16 = torch.empty((rows, ng), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    stages = ["hessian", "prepare", "quantize", "pack"]
+    out = {}
+
+    def step(ev=None):
+        H.zero_()
+        if ev: ev[0].record(stream)
+        gptq.gptq_hessian_accumulate(H, X, ws=ws_h)
+        if ev: ev[1].record(stream)
+        gptq.gptq_prepare_hinv(H, wl.damp, U, dead, status, ws=ws_p, check=False)
+        if ev: ev[2].record(stream)
+        c, sc, z, _, _ = gptq.gptq_quantize_layers(Ws, U, dead, bits=wl.bits,
+                                                   group_size=wl.group_size, sym=wl.sym,
+                                                   block=wl.block, want_loss=False, ws=ws_q)
+        if ev: ev[3].record(stream)
+        gptq.gptq_pack(c, sc, None, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                       qweight=qweight, scales_f16=s16)
+        if ev: ev[4].record(stream)
+        out["c"] = c
+
+    log(f"warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if int(status.item()) != 0:
+        raise RuntimeError("factorization failed during warmup")
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(events[k])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    stage_ms = {st: sum(events[k][i].elapsed_time(events[k][i + 1]) for k in range(args.steps))
+                / args.steps for i, st in enumerate(stages)}
+    # for comparison: the two matrices quantized by separate calls
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for W in Ws:
+        gptq.gptq_quantize_layer(W, U, dead, bits=wl.bits, group_size=wl.group_size, sym=wl.sym,
+                                 block=wl.block, want_loss=False)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    sep_ms = e0.elapsed_time(e1)
+    log(f"{ms_step:.3f} ms/step; stages " + ", ".join(f"{k} {v:.3f} ms" for k, v in stage_ms.items())
+        + f"; separate quantize calls {sep_ms:.3f} ms")
+    syrk_flops = float(n) * d_in * (d_in + 1)
+    tf = syrk_flops / (stage_ms["hessian"] / 1e3) / 1e12
+    line = {
+        "metric": "GPTQ weights quantized/sec/GPU (FFN gate+up 2x11008x4096 sharing one Hessian, "
+                  "131072 tokens)",
+        "value": round(rows * d_in / (ms_step / 1e3), 1),
+        "unit": "weights/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; stands in for a 7B model's FFN weights and calibration tokens)",
+        "config": {"workload": "ffn_gate_up_2x11008x4096_131072tok_3bit_sym_g64",
+                   "d_out": [d_out, d_out], "d_in": d_in, "tokens": n, "bits": wl.bits,
+                   "group_size": wl.group_size, "sym": wl.sym, "block": wl.block},
+        "stage_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "quantize_separate_calls_ms": round(sep_ms, 4),
+        "roofline": {
+            "kernel": "gptq_hessian_accumulate = syrk_bf16_kernel + splitk_reduce_kernel<256>",
+            "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": syrk_flops,
+            "avg_launch_ms": round(stage_ms["hessian"], 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the float64 oracle on a bounded sample (cpu_baseline)")
+        line["cpu_baseline"] = cpu_baseline(wl, synth, n_mats=2)
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--workload", choices=["gptq", "gptq2d", "w4a16"], default="gptq")
+    ap.add_argument("--workload", choices=["gptq", "gptq2d", "w4a16", "ffn_shared"],
+                    default="gptq")
     ap.add_argument("--m", type=int, default=4096, help="rows of X for --workload w4a16")
     ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
     ap.add_argument("--act-order", action="store_true",
@@ -294,6 +404,9 @@ def main():
         return
     if args.workload == "w4a16":
         bench_w4a16(args)
+        return
+    if args.workload == "ffn_shared":
+        bench_shared(args)
         return
 
     import torch

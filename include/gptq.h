@@ -215,6 +215,29 @@ int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t 
 size_t gptq_quantize_perm_workspace(int64_t d_out, int64_t d_in, int block);
 
 /* ---------------------------------------------------------------------------
+ * Several layers that share one Hessian (their inputs are the same
+ * activations, e.g. the query/key/value projections, or the gate and up
+ * projections of a feed-forward block), quantized in one call:
+ * gptq_quantize_layer on the row-wise stack of the matrices.  Rows are
+ * independent given U, so each layer's results are bit-identical to its own
+ * gptq_quantize_layer call.
+ *
+ * W_list       HOST array of count device pointers, matrix i [d_out_list[i] x d_in]
+ *              (all of dtype w_dtype).
+ * d_out_list   HOST array of count row counts (0 allowed).
+ * codes, scales, zeros, loss_rows: stacked outputs over all rows, matrix 0
+ *              first ([sum d_out x d_in] codes, [sum d_out x n_groups]
+ *              scales/zeros, [sum d_out] losses; loss_rows may be NULL).
+ * ws           gptq_quantize_workspace(sum d_out, d_in, block) bytes.
+ * Other arguments and errors as gptq_quantize_layer; 1 <= count <= 64.
+ * ------------------------------------------------------------------------- */
+int gptq_quantize_layers(const void* const* W_list, const int64_t* d_out_list, int count,
+                         int w_dtype, int64_t d_in, const float* U, const uint8_t* dead, int bits,
+                         int group_size, int sym, int block, uint8_t* codes, float* scales,
+                         float* zeros, float* loss_rows, void* ws, size_t ws_bytes,
+                         gptq_stream stream);
+
+/* ---------------------------------------------------------------------------
  * Dequantized product with the packed 4-bit weights (W4A16).
  * "GPTQ：基于近似二阶信息的大模型权重量化", 阶段三 (inference on the integer codes
  * with their group scale and zero) and "GPTQ/AWQ量化中Group Size的精确含义与计算",

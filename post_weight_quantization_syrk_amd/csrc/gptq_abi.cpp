@@ -164,6 +164,35 @@ int gptq_quantize_layer_perm(const void* W, int w_dtype, int64_t d_out, int64_t 
                                                (hipStream_t)stream));
 }
 
+int gptq_quantize_layers(const void* const* W_list, const int64_t* d_out_list, int count,
+                         int w_dtype, int64_t d_in, const float* U, const uint8_t* dead, int bits,
+                         int group_size, int sym, int block, uint8_t* codes, float* scales,
+                         float* zeros, float* loss_rows, void* ws, size_t ws_bytes,
+                         gptq_stream stream) {
+  if (count < 1 || count > 64 || !W_list || !d_out_list) return GPTQ_EINVAL;
+  if (d_in <= 0 || d_in > 65536) return GPTQ_EINVAL;
+  if (w_dtype != GPTQ_BF16 && w_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (bits != 2 && bits != 3 && bits != 4) return (bits == 8) ? GPTQ_EUNSUPPORTED : GPTQ_EINVAL;
+  if (!valid_group(d_in, group_size)) return GPTQ_EINVAL;
+  if (!supported_group(group_size)) return GPTQ_EUNSUPPORTED;
+  if (sym != 0 && sym != 1) return GPTQ_EINVAL;
+  if (block != 128) return GPTQ_EUNSUPPORTED;
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) {
+    if (d_out_list[i] < 0) return GPTQ_EINVAL;
+    if (d_out_list[i] > 0 && !W_list[i]) return GPTQ_EINVAL;
+    rows += d_out_list[i];
+  }
+  if (rows == 0) return GPTQ_OK;
+  if (rows > (int64_t)1 << 31) return GPTQ_EINVAL;
+  if (!U || !codes || !scales || !zeros) return GPTQ_EINVAL;
+  if (ws_bytes < gptq::quantize_workspace(rows, d_in, block) || !ws || !aligned256(ws))
+    return GPTQ_EINVAL;
+  return hip_status(gptq::quantize_multi_launch(W_list, d_out_list, count, w_dtype, d_in, U, dead,
+                                                bits, group_size, sym, codes, scales, zeros,
+                                                loss_rows, ws, (hipStream_t)stream));
+}
+
 int gptq_w4a16_matmul(const void* X, int64_t m, int64_t ldx, const uint32_t* qweight,
                       const uint16_t* scales_f16, const uint16_t* zeros_f16, int64_t d_out,
                       int64_t d_in, int group_size, int sym, float* Y, gptq_stream stream) {

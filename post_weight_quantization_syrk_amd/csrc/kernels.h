@@ -31,6 +31,14 @@ hipError_t prepare_launch(float* H, int64_t d, double damp, float* U, uint8_t* d
 hipError_t prepare_perm_launch(float* H, int64_t d, double damp, const int32_t* perm, float* U,
                                uint8_t* dead, int32_t* dev_status, void* ws, hipStream_t stream);
 
+// Several weight matrices that share U (one Hessian), stacked by rows in
+// order; outputs stacked the same way.
+hipError_t quantize_multi_launch(const void* const* Ws, const int64_t* d_outs, int count,
+                                 int w_dtype, int64_t d_in, const float* U, const uint8_t* dead,
+                                 int bits, int group_size, int sym, uint8_t* codes,
+                                 float* scales, float* zeros, float* loss_rows, void* ws,
+                                 hipStream_t stream);
+
 // ---- activation order: perm = columns by ascending sum_t |x_t,c| ----------
 size_t act_order_workspace(int64_t d, int64_t n_tokens);
 hipError_t act_order_launch(const void* X, int x_dtype, int64_t n_tokens, int64_t ldx, int64_t d,

@@ -560,13 +560,23 @@ hipError_t quantize_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_
                               sym, codes, scales, zeros, nullptr, loss_rows, ws, stream);
 }
 
-hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
-                                const float* U, const uint8_t* dead, const int32_t* perm,
-                                int static_groups, int bits, int group_size, int sym,
-                                uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
-                                float* loss_rows, void* ws, hipStream_t stream) {
+namespace {
+
+// Rows of the working copy come from one or more weight matrices (stacked in
+// order); with several, the columns are in natural order and groups dynamic.
+struct WSource {
+  const void* const* ptrs;
+  const int64_t* rows;
+  int count;
+};
+
+hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t d_in,
+                         const float* U, const uint8_t* dead, const int32_t* perm,
+                         int static_groups, int bits, int group_size, int sym, uint8_t* codes,
+                         float* scales, float* zeros, int32_t* g_idx, float* loss_rows, void* ws,
+                         hipStream_t stream) {
   QuantWs w = carve(ws, d_out, d_in);
-  const int64_t total = d_out * d_in;
+  const void* W = src.ptrs[0];
   // with a permutation the column loop writes codes in processing order to
   // the workspace; they are put back in natural order at the end
   uint8_t* codes_k = perm ? (uint8_t*)ws + quantize_workspace(d_out, d_in, QB) : codes;
@@ -575,11 +585,18 @@ hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64
     hipLaunchKernelGGL(qinit_perm_kernel, pgrid, dim3(256), 0, stream, W, w_dtype, d_out, d_in,
                        dead, perm, w.Wc);
   } else {
-    const int vec = (d_in % 8 == 0) && ((uintptr_t)W % 16 == 0);
-    const unsigned grid =
-        (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
-    hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, W, w_dtype, d_out, d_in,
-                       dead, w.Wc, vec);
+    int64_t r0 = 0;
+    for (int i = 0; i < src.count; ++i) {
+      const int64_t rows = src.rows[i];
+      if (rows == 0) continue;
+      const int64_t total = rows * d_in;
+      const int vec = (d_in % 8 == 0) && ((uintptr_t)src.ptrs[i] % 16 == 0);
+      const unsigned grid =
+          (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
+      hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, src.ptrs[i], w_dtype,
+                         rows, d_in, dead, w.Wc + r0 * d_in, vec);
+      r0 += rows;
+    }
   }
   QSpec q;
   q.maxq = (1 << bits) - 1;
@@ -638,6 +655,30 @@ hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64
                        dim3(256), 0, stream, perm, d_in, q.gsize, q.gshift, static_groups ? 1 : 0,
                        g_idx);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t quantize_perm_launch(const void* W, int w_dtype, int64_t d_out, int64_t d_in,
+                                const float* U, const uint8_t* dead, const int32_t* perm,
+                                int static_groups, int bits, int group_size, int sym,
+                                uint8_t* codes, float* scales, float* zeros, int32_t* g_idx,
+                                float* loss_rows, void* ws, hipStream_t stream) {
+  const WSource src{&W, &d_out, 1};
+  return quantize_core(src, w_dtype, d_out, d_in, U, dead, perm, static_groups, bits, group_size,
+                       sym, codes, scales, zeros, g_idx, loss_rows, ws, stream);
+}
+
+hipError_t quantize_multi_launch(const void* const* Ws, const int64_t* d_outs, int count,
+                                 int w_dtype, int64_t d_in, const float* U, const uint8_t* dead,
+                                 int bits, int group_size, int sym, uint8_t* codes,
+                                 float* scales, float* zeros, float* loss_rows, void* ws,
+                                 hipStream_t stream) {
+  int64_t rows = 0;
+  for (int i = 0; i < count; ++i) rows += d_outs[i];
+  const WSource src{Ws, d_outs, count};
+  return quantize_core(src, w_dtype, rows, d_in, U, dead, nullptr, 0, bits, group_size, sym,
+                       codes, scales, zeros, nullptr, loss_rows, ws, stream);
 }
 
 hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* zeros,

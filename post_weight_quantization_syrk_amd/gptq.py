@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
         "gptq_pack": (I, [P, P, P, I64, I64, I, I, I, P, P, P, P]),
         "gptq2d_round": (I, [P, P, P, I64, P, P, SZ, P]),
         "gptq_w4a16_matmul": (I, [P, I64, I64, P, P, P, I64, I64, I, I, P, P]),
+        "gptq_quantize_layers": (I, [P, P, I, I, I64, P, P, I, I, I, I, P, P, P, P, P, SZ, P]),
         "gptq_act_order": (I, [P, I, I64, I64, I64, P, P, P, SZ, P]),
         "gptq_act_order_workspace": (SZ, [I64, I64]),
         "gptq_prepare_hinv_perm": (I, [P, I64, D, P, P, P, P, P, SZ, P]),
@@ -194,6 +195,44 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, dead: torch.Tensor | N
                                      _ptr(scales), _ptr(zeros), _ptr(loss_rows), _ptr(ws),
                                      nbytes, _stream(stream)), "gptq_quantize_layer")
     return codes, scales, zeros, loss_rows
+
+
+# -------------------------------------------------- layers sharing one Hessian
+def gptq_quantize_layers(Ws: list, U: torch.Tensor, dead: torch.Tensor | None = None, *,
+                         bits: int = 4, group_size: int = 128, sym: bool = False,
+                         block: int = 128, want_loss: bool = True, ws=None, stream=None):
+    """Quantize several matrices [d_out_i, d_in] that share U in one call.  Returns
+    (codes, scales, zeros, loss_rows) stacked by rows in list order, and the list of
+    per-matrix row slices."""
+    if not Ws:
+        raise ValueError("no matrices")
+    d_in = Ws[0].shape[1]
+    dt = _dtype_code(Ws[0])
+    for w in Ws:
+        if w.dim() != 2 or w.shape[1] != d_in or not w.is_contiguous() or _dtype_code(w) != dt:
+            raise ValueError("matrices must be contiguous [d_out_i, d_in] of one dtype")
+    dev = Ws[0].device
+    rows = [int(w.shape[0]) for w in Ws]
+    total = sum(rows)
+    ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
+    codes = torch.empty((total, d_in), dtype=torch.uint8, device=dev)
+    scales = torch.empty((total, max(ng, 1)), dtype=torch.float32, device=dev)
+    zeros = torch.empty((total, max(ng, 1)), dtype=torch.float32, device=dev)
+    loss_rows = torch.empty(total, dtype=torch.float32, device=dev) if want_loss else None
+    if ws is None:
+        ws = _workspace(gptq_quantize_workspace(total, d_in, block), dev)
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    ptrs = (ctypes.c_void_p * len(Ws))(*[w.data_ptr() for w in Ws])
+    dl = (ctypes.c_int64 * len(Ws))(*rows)
+    _check(lib().gptq_quantize_layers(ptrs, dl, len(Ws), dt, d_in, _ptr(U), _ptr(dead), bits,
+                                      group_size, int(bool(sym)), block, _ptr(codes),
+                                      _ptr(scales), _ptr(zeros), _ptr(loss_rows), _ptr(ws),
+                                      nbytes, _stream(stream)), "gptq_quantize_layers")
+    offs, slices = 0, []
+    for r in rows:
+        slices.append(slice(offs, offs + r))
+        offs += r
+    return codes, scales, zeros, loss_rows, slices
 
 
 # -------------------------------------------------- activation ordering

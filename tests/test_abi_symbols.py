@@ -114,3 +114,13 @@ def test_argument_errors_return_before_any_launch():
     assert w(fake, 4, 256, fake, fake, None, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL      # zeros needed
     assert w(P(0x1008), 4, 256, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_EINVAL  # unaligned X
     assert w(fake, 0, 256, fake, fake, fake, 8, 256, 128, 0, fake, None) == gptq.GPTQ_OK         # no rows
+    # layers sharing one Hessian
+    ql = L.gptq_quantize_layers
+    one = (P * 1)(fake)
+    rows = (ctypes.c_int64 * 1)(4)
+    assert ql(one, rows, 0, 0, 256, fake, None, 4, 128, 0, 128, fake, fake, fake, None, fake, 1 << 30, None) == gptq.GPTQ_EINVAL
+    assert ql(one, rows, 1, 0, 256, fake, None, 5, 128, 0, 128, fake, fake, fake, None, fake, 1 << 30, None) == gptq.GPTQ_EINVAL
+    assert ql(one, rows, 1, 0, 256, fake, None, 4, 128, 0, 64, fake, fake, fake, None, fake, 1 << 30, None) == gptq.GPTQ_EUNSUPPORTED
+    assert ql(one, rows, 1, 0, 256, fake, None, 4, 128, 0, 128, fake, fake, fake, None, fake, 16, None) == gptq.GPTQ_EINVAL
+    zero_rows = (ctypes.c_int64 * 1)(0)
+    assert ql(one, zero_rows, 1, 0, 256, fake, None, 4, 128, 0, 128, fake, fake, fake, None, None, 0, None) == gptq.GPTQ_OK
