@@ -61,7 +61,7 @@ def _zero_near_tie(zg, zr, raw):
 
 def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H0=None,
                   max_code_frac: float = 0.005, loss_rtol: float = 1e-3,
-                  max_row_frac: float = 0.05) -> dict:
+                  max_row_frac: float = 0.05, max_param_frac: float = 0.01) -> dict:
     """Check GPU quantizer outputs against the oracle's; returns a report dict.
 
     gpu: codes, scales, zeros (numpy).  ref: the oracle's gptq() result.
@@ -132,7 +132,7 @@ def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H
         problems.append("code differs by more than 1 under identical group parameters")
     if rep["moved_group_max_steps"] > 2.0 + 1e-6:
         problems.append("dequantized value off by more than two steps in a moved group")
-    if rep["param_mismatch"] > 0.01 * rep["groups"]:
+    if rep["param_mismatch"] > max_param_frac * rep["groups"]:
         problems.append("too many groups with moved parameters")
     if rep["code_diff_frac"] > max_code_frac:
         problems.append("too many differing codes")
