@@ -388,6 +388,10 @@ def main():
     ap.add_argument("--workload", choices=["gptq", "gptq2d", "w4a16", "ffn_shared"],
                     default="gptq")
     ap.add_argument("--m", type=int, default=4096, help="rows of X for --workload w4a16")
+    ap.add_argument("--layer", choices=["attn7b", "l70b_sq", "l70b_up"], default="attn7b",
+                    help="layer of the default workload: the 7B attention projection (4096 x "
+                         "4096, 262144 tokens), or the 70B-shaped 8192 x 8192 / 28672 x 8192 "
+                         "layers (65536 tokens)")
     ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
     ap.add_argument("--act-order", action="store_true",
                     help="columns in activation order (gptq_act_order + the *_perm calls)")
@@ -412,7 +416,7 @@ def main():
     import torch
     from post_weight_quantization_syrk_amd import gptq, synth
 
-    wl = synth.ATTN7B
+    wl = {"attn7b": synth.ATTN7B, "l70b_sq": synth.L70B_SQ, "l70b_up": synth.L70B_UP}[args.layer]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     gptq.lib()
@@ -519,7 +523,7 @@ def main():
     }
     upd_tflops = (syrk_flops + trail_flops) / ((stage_ms["hessian"] + stage_ms["quantize"]) / 1e3) / 1e12
     line = {
-        "metric": "GPTQ weights quantized/sec/GPU (4096x4096, 262144 tokens)",
+        "metric": f"GPTQ weights quantized/sec/GPU ({d_out}x{d_in}, {n} tokens)",
         "value": round(value, 1),
         "unit": "weights/s",
         "n_gpus": 1,
@@ -530,7 +534,10 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic (seeded; stands in for a 7B model's weights and 128x2048 calibration tokens)",
+        "data": ("synthetic (seeded; stands in for a 7B model's weights and 128x2048 calibration "
+                 "tokens)" if args.layer == "attn7b" else
+                 "synthetic (seeded; stands in for a 70B model's layer weights and 65536 calibration "
+                 "tokens)"),
         "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "tokens": n,
                    "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym,
                    "block": wl.block, "damp": wl.damp, "act_order": bool(order),
