@@ -10,15 +10,16 @@
 //              (DPP row broadcast), every lane takes the same rounding decision,
 //              and each lane applies the feedback to its own 8 columns.  Group
 //              min/max come from a 16-lane butterfly at the group's first column.
-//   trailing : W[:, later columns] -= Err U, an fp32 MFMA GEMM
-//              (v_mfma_f32_32x32x2f32).  Blocks go in groups of four: after
+//   trailing : W[:, later columns] -= Err U on the bf16 matrix cores, the
+//              fp32 operands split into bf16 hi + lo and the product formed
+//              in three passes (trailing3_kernel).  Blocks go in groups of four: after
 //              each block, its errors update the rest of its group (K = 128);
 //              after the group, all four blocks' errors update every column
 //              after it at once (K = 512), so the bulk of W is read and
 //              written once per group.
 #include "common.h"
 #include "kernels.h"
-#include "mfma_f32.h"
+#include "mfma_f32.h"  // StaticFor
 
 #include <hip/hip_fp16.h>
 #include <algorithm>
@@ -436,78 +437,129 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:n1] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:n1]  (fp32 MFMA, TM x 64
-// tiles).  The tile of Wc is loaded into the accumulators first and the error
-// operand is negated on its way into LDS, so the products accumulate onto Wc
-// and the final store needs no read.  K runs in chunks of 32 (29 KiB of LDS
-// for TM = 128), the next chunk's loads in flight while the current one
-// multiplies; three workgroups share a CU, one's loads and stores overlapping
-// the others' matrix products.
-constexpr int TKC = 32;  // K chunk
+// Wc[:, n0:n1] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
+// cores: each fp32 operand is split into bf16 hi + lo (hi the nearest bf16,
+// lo the nearest bf16 of the exact remainder) and the product is formed as
+// lo*hi + hi*lo + hi*hi with v_mfma_f32_32x32x16_bf16 into fp32 accumulators,
+// which keeps about 16 significant bits of every product (the dropped lo*lo
+// term and the rounding of lo are below 2^-16 relative); the errors it leaves
+// in the feedback are far below a quantization step.  TM x 64 tiles, K in
+// chunks of 32 (two MFMA steps of 16).  The negated error tile is stored
+// row-major (k contiguous), the U tile transposed (n-major, k contiguous), so
+// every lane reads its 8 consecutive k as 16 bytes; row pitches of 80 bytes
+// keep those reads free of bank conflicts.  The Wc tile is loaded into the
+// accumulators first and stored back at the end.
+constexpr int T3K = 32;           // k per chunk
+constexpr int T3P = T3K + 8;      // LDS row pitch (bf16 elements): 80 bytes
+
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
 
 template <int TM>
-__global__ __launch_bounds__(256, 3) void trailing_kernel(float* __restrict__ Wc,
-                                                       const float* __restrict__ Err,
-                                                       const float* __restrict__ U,
-                                                       int64_t d_out, int64_t d_in, int64_t b0,
-                                                       int kb, int64_t n0, int64_t n1) {
+__global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
+                                                        const float* __restrict__ Err,
+                                                        const float* __restrict__ U,
+                                                        int64_t d_out, int64_t d_in, int64_t b0,
+                                                        int kb, int64_t n0, int64_t n1) {
   constexpr int TN = 64;
-  using TrailTile = MfmaTile<TM, TN, TKC, false>;
-  constexpr int NP = TM * TKC / 256, NQ = TKC * TN / 256;
-  __shared__ __attribute__((aligned(16))) float lds[TrailTile::lds_floats];
+  constexpr int NBLK = (TM / 32) * (TN / 32) / 4;  // 32 x 32 blocks per wave
+  constexpr int NP = TM * T3K / 256, NQ = T3K * TN / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], al[TM * T3P];
+  __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bl[TN * T3P];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int h = lane >> 5, l32 = lane & 31;
   const int64_t ncols = n1 - n0;
   const int ntn = (int)ceil_div(ncols, TN);
   const int64_t m0 = (int64_t)(blockIdx.x / ntn) * TM;
   const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * TN;
   const int rows = (int)min<int64_t>(TM, d_out - m0);
   const int cols = (int)min<int64_t>(TN, n1 - n0t);
-  f32x16 acc[TrailTile::FM][TrailTile::FN];
+  // this wave's blocks: (bm, bn) with bm = row block, bn = column block
+  int bm[NBLK], bn[NBLK];
+#pragma unroll
+  for (int q = 0; q < NBLK; ++q) {
+    const int blk = wave * NBLK + q;  // row-block major over (TM / 32) x 2
+    bm[q] = blk >> 1;
+    bn[q] = blk & 1;
+  }
   float* C = Wc + m0 * d_in + n0t;
-  // the tile of Wc into the accumulators (clamped addresses; masked at the store)
-  TrailTile::set_each(acc, [&](int row, int col) {
-    return C[(int64_t)(row < rows ? row : rows - 1) * d_in + (col < cols ? col : cols - 1)];
-  });
+  f32x16 acc[NBLK];
+#pragma unroll
+  for (int q = 0; q < NBLK; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
+      const int c = 32 * bn[q] + l32;
+      acc[q][i] = C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
+    }
   const float* P = Err + m0 * d_in + b0;
   const float* Q = U + b0 * d_in + n0t;
   float vp[NP], vq[NQ];
   auto gload = [&](int kc) __attribute__((always_inline)) {
-    const int kn = min(TKC, kb - kc);
+    const int kn = min(T3K, kb - kc);
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      const int e = u * 256 + threadIdx.x, r = e / TKC, c = e % TKC;
+      const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
       vp[u] = P[(int64_t)(r < rows ? r : rows - 1) * d_in + kc + (c < kn ? c : kn - 1)];
     }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int e = u * 256 + threadIdx.x, r = e / TN, c = e % TN;
+      const int e = u * 256 + tid, r = e / TN, c = e % TN;
       vq[u] = Q[(int64_t)(kc + (r < kn ? r : kn - 1)) * d_in + (c < cols ? c : cols - 1)];
     }
   };
   auto lstore = [&](int kc) __attribute__((always_inline)) {
-    const int kn = min(TKC, kb - kc);
+    const int kn = min(T3K, kb - kc);
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-      const int e = u * 256 + threadIdx.x, r = e / TKC, c = e % TKC;
-      lds[r * TrailTile::PP + c] = (r < rows && c < kn) ? -vp[u] : 0.0f;
+      const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
+      const float x = (r < rows && c < kn) ? -vp[u] : 0.0f;
+      const uint16_t hi = bf16_rne_bits(x);
+      ah[r * T3P + c] = hi;
+      al[r * T3P + c] = bf16_rne_bits(x - bf16_bits_to_f32(hi));
     }
-    float* lq = lds + TM * TrailTile::PP;
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
-      const int e = u * 256 + threadIdx.x, r = e / TN, c = e % TN;
-      lq[r * TrailTile::QPITCH + c] = (r < kn && c < cols) ? vq[u] : 0.0f;
+      const int e = u * 256 + tid, r = e / TN, c = e % TN;  // r = k, c = n
+      const float x = (r < kn && c < cols) ? vq[u] : 0.0f;
+      const uint16_t hi = bf16_rne_bits(x);
+      bh[c * T3P + r] = hi;
+      bl[c * T3P + r] = bf16_rne_bits(x - bf16_bits_to_f32(hi));
     }
   };
   gload(0);
-  for (int kc = 0; kc < kb; kc += TKC) {
+  for (int kc = 0; kc < kb; kc += T3K) {
     if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
     lstore(kc);
     __syncthreads();
-    if (kc + TKC < kb) gload(kc + TKC);
-    TrailTile::mma(lds, acc);
+    if (kc + T3K < kb) gload(kc + T3K);
+#pragma unroll
+    for (int ks = 0; ks < T3K / 16; ++ks) {
+      const int ko = 16 * ks + 8 * h;
+#pragma unroll
+      for (int q = 0; q < NBLK; ++q) {
+        const int ar = (32 * bm[q] + l32) * T3P + ko, br = (32 * bn[q] + l32) * T3P + ko;
+        const bf16x8 a_h = *(const bf16x8*)(ah + ar), a_l = *(const bf16x8*)(al + ar);
+        const bf16x8 b_h = *(const bf16x8*)(bh + br), b_l = *(const bf16x8*)(bl + br);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_l, b_h, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_l, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_h, acc[q], 0, 0, 0);
+      }
+    }
   }
-  TrailTile::for_each(acc, [&](int row, int col, float v) {
-    if (row < rows && col < cols) C[(int64_t)row * d_in + col] = v;
-  });
+#pragma unroll
+  for (int q = 0; q < NBLK; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
+      const int c = 32 * bn[q] + l32;
+      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = acc[q][i];
+    }
 }
 
 // ---- pack -------------------------------------------------------------------
@@ -634,13 +686,13 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        hipLaunchKernelGGL(trailing_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, stream,
+        hipLaunchKernelGGL(trailing3_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, stream,
                            w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
       }
     }
     if (gcol < d_in) {  // every block of the group is full
       const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
-      hipLaunchKernelGGL(trailing_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
+      hipLaunchKernelGGL(trailing3_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
                          (const float*)w.Err, U, d_out, d_in, g0 * QB, (int)(gcol - g0 * QB),
                          gcol, d_in);
     }

@@ -61,7 +61,8 @@ def _zero_near_tie(zg, zr, raw):
 
 def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H0=None,
                   max_code_frac: float = 0.005, loss_rtol: float = 1e-3,
-                  max_row_frac: float = 0.05, max_param_frac: float = 0.01) -> dict:
+                  max_row_frac: float = 0.05, max_param_frac: float = 0.01,
+                  max_moved_steps: float = 2.5) -> dict:
     """Check GPU quantizer outputs against the oracle's; returns a report dict.
 
     gpu: codes, scales, zeros (numpy).  ref: the oracle's gptq() result.
@@ -130,8 +131,12 @@ def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H
         problems.append("code out of range")
     if rep["code_max_diff"] > 1:
         problems.append("code differs by more than 1 under identical group parameters")
-    if rep["moved_group_max_steps"] > 2.0 + 1e-6:
-        problems.append("dequantized value off by more than two steps in a moved group")
+    # a moved group lies after the row's first (admissible) divergence: the two
+    # sides' values come from different greedy paths, each within half a step
+    # of its own compensated weight; 2.5 steps is a sanity bound, not an
+    # arithmetic one
+    if rep["moved_group_max_steps"] > max_moved_steps:
+        problems.append("dequantized value off by more than max_moved_steps in a moved group")
     if rep["param_mismatch"] > max_param_frac * rep["groups"]:
         problems.append("too many groups with moved parameters")
     if rep["code_diff_frac"] > max_code_frac:
