@@ -424,15 +424,32 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     w[7] = fmaf(-delta, u1.w, w[7]);
   });
   if (!live) return;
-  // codes and scaled errors of this lane's 8 columns
+  // codes and scaled errors of this lane's 8 columns (the errors as two
+  // 16-byte stores when the lane's columns are all inside and 16-byte aligned:
+  // d_in a multiple of 4, b0 a multiple of 128)
+  // (the codes as one 8-byte store when d_in is a multiple of 8 and codes is
+  // 8-byte aligned)
   uint8_t* cdst = codes + rr * d_in + b0 + 8 * c;
   float* edst = Err + rr * d_in + b0 + 8 * c;
+  if ((d_in & 7) == 0 && ((uintptr_t)codes & 7) == 0 && 8 * c + 8 <= bw) {
+    uint32_t cw[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    if (8 * c + i < bw) {
-      cdst[i] = (uint8_t)cr[i];
-      edst[i] = er[i];
-    }
+    for (int t = 0; t < 2; ++t)
+      cw[t] = (uint32_t)cr[4 * t] | ((uint32_t)cr[4 * t + 1] << 8) |
+              ((uint32_t)cr[4 * t + 2] << 16) | ((uint32_t)cr[4 * t + 3] << 24);
+    *(uint2*)cdst = make_uint2(cw[0], cw[1]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * c + i < bw) cdst[i] = (uint8_t)cr[i];
+  }
+  if ((d_in & 3) == 0 && 8 * c + 8 <= bw) {
+    ((float4*)edst)[0] = make_float4(er[0], er[1], er[2], er[3]);
+    ((float4*)edst)[1] = make_float4(er[4], er[5], er[6], er[7]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if (8 * c + i < bw) edst[i] = er[i];
   }
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
