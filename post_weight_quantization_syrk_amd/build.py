@@ -26,12 +26,17 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
 ]
+# Per-file additions.  The W4A16 product rescales its group accumulators with
+# plain VALU arithmetic; MFMA results kept in ordinary VGPRs spare the moves
+# to and from the accumulation registers around every rescale.
+FILE_FLAGS = {"w4a16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o",
+           obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

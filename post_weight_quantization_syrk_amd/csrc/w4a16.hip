@@ -39,14 +39,22 @@ __device__ __forceinline__ float f16_bits_to_float(uint16_t b) {
   return __half2float(__ushort_as_half(b));
 }
 
-// the 8 codes of a word minus the zero, as exact bf16 integers, k order kept
+// the 8 codes of a word minus the zero, as exact bf16 integers, k order kept:
+// the even codes go to the bytes of one register and the odd ones to the
+// bytes of another, so each code converts to float straight from its byte
+// (the empty asm keeps the masks from being folded into per-code bit-field
+// extracts, so the conversions select the byte themselves), and each pair's
+// two upper halves (exact: small integers) are joined with one byte permute
 __device__ __forceinline__ bf16x8 dequant_word(uint32_t w, float z) {
+  uint32_t ev = w & 0x0f0f0f0fu, od = (w >> 4) & 0x0f0f0f0fu;
+  asm("" : "+v"(ev), "+v"(od));
   uint32_t o[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float lo = (float)((w >> (8 * j)) & 15u) - z;
-    const float hi = (float)((w >> (8 * j + 4)) & 15u) - z;
-    o[j] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+    const float lo = (float)((ev >> (8 * j)) & 0xffu) - z;
+    const float hi = (float)((od >> (8 * j)) & 0xffu) - z;
+    // bytes 2, 3 of lo, then bytes 2, 3 of hi
+    o[j] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
   bf16x8 r;
   __builtin_memcpy(&r, o, sizeof(r));
@@ -129,19 +137,24 @@ __global__ __launch_bounds__(256) void w4a16_kernel(const uint16_t* __restrict__
       const uint32_t word = wb[4 * (kk >> 1) + (kk & 1)];
       const bf16x8 bv = dequant_word(word, z);
       const int koff = 32 * (kk >> 1) + 16 * h + 8 * (kk & 1);
+      bf16x8 av[4];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        const bf16x8 av = *(const bf16x8*)(xb + (32 * mi + l32) * XP + koff);
-        acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[mi], 0, 0, 0);
+      for (int mi = 0; mi < 4; ++mi) av[mi] = *(const bf16x8*)(xb + (32 * mi + l32) * XP + koff);
+      if (k0 % G == 0) {  // a group's first products start from zero
+        const f32x16 zero = {};
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mi], bv, zero, 0, 0, 0);
+      } else {
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+          acc[mi] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mi], bv, acc[mi], 0, 0, 0);
       }
       if ((k0 + 16) % G == 0) {  // the group ends: scale it into the total
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            tot[mi][i] = fmaf(s, acc[mi][i], tot[mi][i]);
-            acc[mi][i] = 0.0f;
-          }
+          for (int i = 0; i < 16; ++i) tot[mi][i] = fmaf(s, acc[mi][i], tot[mi][i]);
       }
     }
     if (c + 1 < nch) {
