@@ -476,8 +476,23 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
+// The same split for a pair, with the hardware's nearest-even conversion of
+// two floats at once: hi parts packed low-first, lo parts likewise into lo.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& lo) {
+  const f32x2v x = {x0, x1};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
+  const f32x2v hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xffff0000u)};
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hf, bf16x2v));
+  return hb;
+}
 
-template <int TM>
+// VEC (d_in a multiple of 4, U 16-byte aligned; the launches give kb a
+// multiple of 32 and b0, n0 multiples of 64): each thread loads 4 consecutive
+// k of an error row and 2 k rows x 4 columns of U as 16-byte vectors, and
+// splits and stores them in pairs of k.
+template <int TM, bool VEC>
 __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
                                                         const float* __restrict__ Err,
                                                         const float* __restrict__ U,
@@ -517,8 +532,25 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
   const float* P = Err + m0 * d_in + b0;
   const float* Q = U + b0 * d_in + n0t;
   float vp[NP], vq[NQ];
+  static_assert(NQ == 8 && NP % 4 == 0, "vector staging takes 2 x 4 U values per thread");
+  const int vn = 4 * (tid & 15), vk = 2 * (tid >> 4);  // VEC: this thread's U columns, k pair
   auto gload = [&](int kc) __attribute__((always_inline)) {
     const int kn = min(T3K, kb - kc);
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < NP / 4; ++j) {
+        const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
+        const float4 v =
+            *(const float4*)(P + (int64_t)(r < rows ? r : rows - 1) * d_in + kc + c);
+        vp[4 * j] = v.x; vp[4 * j + 1] = v.y; vp[4 * j + 2] = v.z; vp[4 * j + 3] = v.w;
+      }
+      const int nc = vn < cols ? vn : 0;
+      const float4 v0 = *(const float4*)(Q + (int64_t)(kc + vk) * d_in + nc);
+      const float4 v1 = *(const float4*)(Q + (int64_t)(kc + vk + 1) * d_in + nc);
+      vq[0] = v0.x; vq[1] = v0.y; vq[2] = v0.z; vq[3] = v0.w;
+      vq[4] = v1.x; vq[5] = v1.y; vq[6] = v1.z; vq[7] = v1.w;
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
@@ -532,6 +564,27 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
   };
   auto lstore = [&](int kc) __attribute__((always_inline)) {
     const int kn = min(T3K, kb - kc);
+    if constexpr (VEC) {
+#pragma unroll
+      for (int j = 0; j < NP / 4; ++j) {
+        const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
+        const bool ok = r < rows;
+        uint32_t l0, l1;
+        const uint32_t h0 = split_pair(ok ? -vp[4 * j] : 0.0f, ok ? -vp[4 * j + 1] : 0.0f, l0);
+        const uint32_t h1 = split_pair(ok ? -vp[4 * j + 2] : 0.0f, ok ? -vp[4 * j + 3] : 0.0f, l1);
+        *(uint2*)(ah + r * T3P + c) = make_uint2(h0, h1);
+        *(uint2*)(al + r * T3P + c) = make_uint2(l0, l1);
+      }
+      const bool ok = vn < cols;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        uint32_t l;
+        const uint32_t hw = split_pair(ok ? vq[t] : 0.0f, ok ? vq[4 + t] : 0.0f, l);
+        *(uint32_t*)(bh + (vn + t) * T3P + vk) = hw;
+        *(uint32_t*)(bl + (vn + t) * T3P + vk) = l;
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
@@ -688,6 +741,8 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // of the group's errors go to the columns after it at once (far update,
   // K = 128 QG), so the bulk of W is read and written once per group.
   const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
+  static_assert(QB % T3K == 0, "trailing updates take whole chunks");
+  const bool tvec = (d_in % 4 == 0) && ((uintptr_t)U % 16 == 0);
   const int64_t nb = ceil_div(d_in, QB);
   for (int64_t g0 = 0; g0 < nb; g0 += QG) {
     const int64_t gend = std::min<int64_t>(nb, g0 + QG);
@@ -703,15 +758,25 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        hipLaunchKernelGGL(trailing3_kernel<64>, dim3((unsigned)tiles), dim3(256), 0, stream,
-                           w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
+        if (tvec)
+          hipLaunchKernelGGL((trailing3_kernel<64, true>), dim3((unsigned)tiles), dim3(256), 0,
+                             stream, w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
+        else
+          hipLaunchKernelGGL((trailing3_kernel<64, false>), dim3((unsigned)tiles), dim3(256), 0,
+                             stream, w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
       }
     }
     if (gcol < d_in) {  // every block of the group is full
       const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
-      hipLaunchKernelGGL(trailing3_kernel<128>, dim3((unsigned)tiles), dim3(256), 0, stream, w.Wc,
-                         (const float*)w.Err, U, d_out, d_in, g0 * QB, (int)(gcol - g0 * QB),
-                         gcol, d_in);
+      const int kb = (int)(gcol - g0 * QB);
+      if (tvec)
+        hipLaunchKernelGGL((trailing3_kernel<128, true>), dim3((unsigned)tiles), dim3(256), 0,
+                           stream, w.Wc, (const float*)w.Err, U, d_out, d_in, g0 * QB, kb, gcol,
+                           d_in);
+      else
+        hipLaunchKernelGGL((trailing3_kernel<128, false>), dim3((unsigned)tiles), dim3(256), 0,
+                           stream, w.Wc, (const float*)w.Err, U, d_out, d_in, g0 * QB, kb, gcol,
+                           d_in);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -370,6 +370,11 @@ def test_e2e_small_workload():
     synth.scaled(synth.FFN_DOWN, d_out=256, d_in=1408, n_tokens=8192, chunk_tokens=4096),
     synth.scaled(synth.L70B_SQ, d_out=300, d_in=1024, n_tokens=8192, bits=2, group_size=32),
     synth.scaled(synth.L70B_SQ, d_out=300, d_in=1024, n_tokens=8192, bits=4, group_size=-1),
+    # d_in not a multiple of 4: the trailing updates stage their operands
+    # element by element (650 = 5 x 128 + 10, ragged last block)
+    synth.scaled(synth.L70B_SQ, d_out=200, d_in=650, n_tokens=4096, bits=4, group_size=-1),
+    # 1028 = 8 x 128 + 4: vector staging with a 4-column last tile
+    synth.scaled(synth.L70B_SQ, d_out=136, d_in=1028, n_tokens=4096, bits=3, group_size=-1),
 ], ids=lambda w: w.name)
 def test_e2e_scaled_workloads(wl):
     _e2e(wl)
