@@ -461,11 +461,13 @@ __global__ __launch_bounds__(256) void colloop_kernel(
 // which keeps about 16 significant bits of every product (the dropped lo*lo
 // term and the rounding of lo are below 2^-16 relative); the errors it leaves
 // in the feedback are far below a quantization step.  TM x 64 tiles, K in
-// chunks of 32 (two MFMA steps of 16).  The negated error tile is stored
-// row-major (k contiguous), the U tile transposed (n-major, k contiguous), so
-// every lane reads its 8 consecutive k as 16 bytes; row pitches of 80 bytes
-// keep those reads free of bank conflicts.  The Wc tile is loaded into the
-// accumulators first and stored back at the end.
+// chunks of 32 (two MFMA steps of 16).  The error tile is stored row-major
+// (k contiguous), the U tile transposed (n-major, k contiguous), so every lane
+// reads its 8 consecutive k as 16 bytes; row pitches of 80 bytes keep those
+// reads free of bank conflicts.  The accumulators start at -Wc and collect
+// Err U, and the tile is stored back negated: negation commutes with every
+// rounding, so this is Wc - Err U as accumulated the other way round, with no
+// negation per staged element.
 constexpr int T3K = 32;           // k per chunk
 constexpr int T3P = T3K + 8;      // LDS row pitch (bf16 elements): 80 bytes
 
@@ -527,7 +529,7 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
       const int c = 32 * bn[q] + l32;
-      acc[q][i] = C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
+      acc[q][i] = -C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
     }
   const float* P = Err + m0 * d_in + b0;
   const float* Q = U + b0 * d_in + n0t;
@@ -565,21 +567,22 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
   auto lstore = [&](int kc) __attribute__((always_inline)) {
     const int kn = min(T3K, kb - kc);
     if constexpr (VEC) {
+      // no masks: every k is inside the block, and rows past d_out or columns
+      // past n1 (clamped copies of finite values) only reach accumulator rows
+      // or columns that are never stored
 #pragma unroll
       for (int j = 0; j < NP / 4; ++j) {
         const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
-        const bool ok = r < rows;
         uint32_t l0, l1;
-        const uint32_t h0 = split_pair(ok ? -vp[4 * j] : 0.0f, ok ? -vp[4 * j + 1] : 0.0f, l0);
-        const uint32_t h1 = split_pair(ok ? -vp[4 * j + 2] : 0.0f, ok ? -vp[4 * j + 3] : 0.0f, l1);
+        const uint32_t h0 = split_pair(vp[4 * j], vp[4 * j + 1], l0);
+        const uint32_t h1 = split_pair(vp[4 * j + 2], vp[4 * j + 3], l1);
         *(uint2*)(ah + r * T3P + c) = make_uint2(h0, h1);
         *(uint2*)(al + r * T3P + c) = make_uint2(l0, l1);
       }
-      const bool ok = vn < cols;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         uint32_t l;
-        const uint32_t hw = split_pair(ok ? vq[t] : 0.0f, ok ? vq[4 + t] : 0.0f, l);
+        const uint32_t hw = split_pair(vq[t], vq[4 + t], l);
         *(uint32_t*)(bh + (vn + t) * T3P + vk) = hw;
         *(uint32_t*)(bl + (vn + t) * T3P + vk) = l;
       }
@@ -588,7 +591,7 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
-      const float x = (r < rows && c < kn) ? -vp[u] : 0.0f;
+      const float x = (r < rows && c < kn) ? vp[u] : 0.0f;
       const uint16_t hi = bf16_rne_bits(x);
       ah[r * T3P + c] = hi;
       al[r * T3P + c] = bf16_rne_bits(x - bf16_bits_to_f32(hi));
@@ -628,7 +631,7 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
       const int c = 32 * bn[q] + l32;
-      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = acc[q][i];
+      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = -acc[q][i];
     }
 }
 
