@@ -286,6 +286,11 @@ __device__ __forceinline__ float row_max(float v) {
   for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
   return v;
 }
+__device__ __forceinline__ float row_sum(float v) {
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 16);
+  return v;
+}
 
 // STATIC: the group parameters are given (static groups, natural groups of
 // the original weights, in scales/zeros) and column k of the block uses those
@@ -349,6 +354,24 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   __syncthreads();
   if (tid < QB) invd[tid] = 1.0f / us[tid * UPITCH + tid];
   __syncthreads();
+  // Row j of the block scaled by 1 / U_jj: column j's feedback is then its
+  // unscaled error x - what times the scaled row, and neither the division
+  // nor its LDS read sits on the chain from one column to the next.  Thread
+  // t scales half t % 2 of row t / 2 (16-byte LDS accesses).
+  {
+    const float sc = invd[tid >> 1];
+    float4* rw = (float4*)(us + (tid >> 1) * UPITCH + 64 * (tid & 1));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float4 v = rw[i];
+      v.x *= sc;
+      v.y *= sc;
+      v.z *= sc;
+      v.w *= sc;
+      rw[i] = v;
+    }
+  }
+  __syncthreads();
 
   GroupParams gp;
   if (q.gsize == 0) {
@@ -360,7 +383,6 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   }
   const int gmask = q.gsize - 1;
   float cr[8], er[8];
-  float loss = 0.0f;
   // U row of the next column, read one column ahead so the LDS latency is off
   // the dependency chain.
   float4 un0 = ((const float4*)(us + 8 * c))[0], un1 = ((const float4*)(us + 8 * c))[1];
@@ -402,11 +424,10 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     const float x = row_bcast<(j >> 3)>(w[j & 7]);
     const float code = quantize_code(x, gp, maxq);
     const float what = gp.s * (code - gp.z);
-    const float delta = (x - what) * invd[j];
-    loss = fmaf(delta, delta, loss);
+    const float e = x - what;
     if (c == (j >> 3)) {
       cr[j & 7] = code;
-      er[j & 7] = delta;
+      er[j & 7] = e;
     }
     const float4 u0 = un0, u1 = un1;
     if constexpr (j + 1 < QB) {
@@ -414,15 +435,25 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       un0 = urow[0];
       un1 = urow[1];
     }
-    w[0] = fmaf(-delta, u0.x, w[0]);
-    w[1] = fmaf(-delta, u0.y, w[1]);
-    w[2] = fmaf(-delta, u0.z, w[2]);
-    w[3] = fmaf(-delta, u0.w, w[3]);
-    w[4] = fmaf(-delta, u1.x, w[4]);
-    w[5] = fmaf(-delta, u1.y, w[5]);
-    w[6] = fmaf(-delta, u1.z, w[6]);
-    w[7] = fmaf(-delta, u1.w, w[7]);
+    w[0] = fmaf(-e, u0.x, w[0]);
+    w[1] = fmaf(-e, u0.y, w[1]);
+    w[2] = fmaf(-e, u0.z, w[2]);
+    w[3] = fmaf(-e, u0.w, w[3]);
+    w[4] = fmaf(-e, u1.x, w[4]);
+    w[5] = fmaf(-e, u1.y, w[5]);
+    w[6] = fmaf(-e, u1.z, w[6]);
+    w[7] = fmaf(-e, u1.w, w[7]);
   });
+  // the scaled errors delta = (x - what) / U_jj of this lane's 8 columns
+  // (columns past the edge have x - what = 0), and the row's loss sum_j
+  // delta_j^2: this lane's 8 terms, then the row's 16 lanes
+  float loss = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    er[i] *= invd[8 * c + i];
+    loss = fmaf(er[i], er[i], loss);
+  }
+  loss = row_sum(loss);
   if (!live) return;
   // codes and scaled errors of this lane's 8 columns (the errors as two
   // 16-byte stores when the lane's columns are all inside and 16-byte aligned:
