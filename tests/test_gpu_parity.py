@@ -467,3 +467,27 @@ def test_70b_shape_layer_sampled_rows():
         rep = compare_quant(sub_out, ref, group_size=g, bits=bits, W=W64[rows], H0=H0r,
                             max_row_frac=1.0, max_code_frac=0.02, max_param_frac=0.1)
         print(f"[70b] bits={bits} g={g} {rep}", flush=True)
+
+
+def test_trailing_staging_paths_agree():
+    """The trailing update loads its operands as 16-byte vectors when d_in is
+    a multiple of 4 and U is 16-byte aligned, and element by element
+    otherwise.  Both feed the same bf16 hi + lo parts to the same products in
+    the same order, so the results agree bit for bit; a copy of U at a 4-byte
+    offset takes the element-wise path on the same layer."""
+    d_out, d_in = 200, 640
+    rng = np.random.default_rng(640)
+    A = rng.standard_normal((d_in + 96, d_in)) * np.exp(0.5 * rng.standard_normal(d_in))
+    H = (2.0 / A.shape[0]) * (A.T @ A)
+    W = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(H))
+    buf = torch.empty(d_in * d_in + 1, dtype=torch.float32, device=DEV)
+    U_off = buf[1:].view(d_in, d_in)
+    U_off.copy_(U)
+    assert U.data_ptr() % 16 == 0 and U_off.data_ptr() % 16 != 0
+    print(f"[staging] {d_out}x{d_in}: aligned U against U at a 4-byte offset", flush=True)
+    for bits, g, sym in [(4, 128, False), (3, -1, True)]:
+        a = _gpu_quant(dev_f32(W), U, dead, bits, g, sym)
+        b = _gpu_quant(dev_f32(W), U_off, dead, bits, g, sym)
+        for key in ("codes", "scales", "zeros", "loss"):
+            np.testing.assert_array_equal(a[key], b[key])
