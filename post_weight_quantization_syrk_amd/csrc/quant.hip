@@ -382,6 +382,14 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     gp.z = zeros[rr];
   }
   const int gmask = q.gsize - 1;
+  // STATIC: the next column's parameters, read one column ahead
+  float ns = 0.0f, ni = 0.0f, nz = 0.0f;
+  if constexpr (STATIC) {
+    const int e = (tid >> 4) * QB;
+    ns = sps[e];
+    ni = spi[e];
+    nz = spz[e];
+  }
   float cr[8], er[8];
   // U row of the next column, read one column ahead so the LDS latency is off
   // the dependency chain.
@@ -394,12 +402,17 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   StaticFor<0, QB>::run([&](auto J) {
     constexpr int j = decltype(J)::value;
     if constexpr (STATIC) {
-      const int e = (tid >> 4) * QB + j;
-      gp.s = sps[e];
-      gp.inv_s = spi[e];
-      gp.z = spz[e];
+      gp.s = ns;
+      gp.inv_s = ni;
+      gp.z = nz;
       gp.hs = 0.5f * gp.s;
       gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
+      if constexpr (j + 1 < QB) {
+        const int e = (tid >> 4) * QB + j + 1;
+        ns = sps[e];
+        ni = spi[e];
+        nz = spz[e];
+      }
     } else if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
       if (q.gsize != 0 && (j & gmask) == 0) {
         const bool mine = (8 * c >= j) && (8 * c < j + q.gsize);
