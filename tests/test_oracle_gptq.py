@@ -4,6 +4,9 @@ Each check ties the oracle to something other than itself: brute force, a
 textbook algorithm computed another way (Gram-Schmidt nearest plane), closed
 forms and exact invariants of the method.  CPU only.
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -266,3 +269,49 @@ def test_pins_catch_planted_mistakes(monkeypatch):
     E = Wd - r["What"]
     quad = np.einsum("ij,jk,ik->i", E, p["H"], E)
     assert not np.allclose(r["loss_damped"], quad, rtol=1e-6)
+
+
+# ------------------------------------------- dynamic groups, worked by hand
+def _hand_example(golden_dir):
+    with open(os.path.join(golden_dir, "dynamic_group_feedback_hand.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.parametrize("block", [None, 2, 4])
+def test_dynamic_group_params_follow_feedback_hand_example(golden_dir, block):
+    """A group's scale and zero come from its values after the feedback of every
+    earlier column: the hand-worked example (dyadic numbers, every step exact)
+    fixes codes, binary16 scales, zeros, W_hat, the scaled errors and their
+    sum of squares bit for bit, sequentially and lazily batched."""
+    g = _hand_example(golden_dir)
+    W, U = np.array(g["W"]), np.array(g["U"])
+    r = oracle.gptq(W, U, bits=g["bits"], group_size=g["group_size"], sym=g["sym"], block=block)
+    np.testing.assert_array_equal(r["codes"], np.array(g["codes"]))
+    np.testing.assert_array_equal(r["scales"], np.array(g["scales"]))
+    np.testing.assert_array_equal(r["zeros"], np.array(g["zeros"]))
+    np.testing.assert_array_equal(r["What"], np.array(g["What"]))
+    np.testing.assert_array_equal(r["delta"], np.array(g["delta"]))
+    np.testing.assert_array_equal(r["loss_damped"], np.array(g["loss_damped"]))
+
+
+def test_group_params_from_original_weights_fail_hand_example(golden_dir):
+    """Planted slip: the oracle's loop with each group's parameters taken from
+    the original weights instead of the compensated ones.  The hand example
+    rejects it (group 1's step becomes 0.375 instead of 0.3125)."""
+    g = _hand_example(golden_dir)
+    W, U = np.array(g["W"]), np.array(g["U"])
+    bits, G = g["bits"], g["group_size"]
+    maxq = oracle.maxq_for(bits)
+    scales = np.zeros((1, W.shape[1] // G))
+    cur = {}
+
+    def qcol_original(j, Wc):
+        if j % G == 0:
+            cur["s"], cur["z"] = oracle.group_params(W[:, j:j + G], bits, False)
+            scales[:, j // G] = cur["s"]
+        return oracle.quantize_values(Wc[:, j], cur["s"], cur["z"], maxq)[1]
+
+    _, What, _ = oracle.column_loop(W, U, qcol_original)
+    np.testing.assert_array_equal(scales, np.array(g["scales_if_from_original_weights"]))
+    assert not np.array_equal(scales, np.array(g["scales"]))
+    assert not np.array_equal(What, np.array(g["What"]))

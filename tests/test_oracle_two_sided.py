@@ -3,11 +3,12 @@
 * The anti-diagonal schedule reproduces the vectorized (Kronecker) nearest
   plane exactly (方法, 核心洞察: same output as the quartic method).
 * Identity bases reduce to plain rounding; a left identity basis reduces each
-  row to one-sided GPTQ on reversed columns, pinned separately against
-  Gram-Schmidt nearest plane in the one-sided tests.
+  row, and a right identity basis each column, to one-sided GPTQ on reversed
+  coordinates, pinned separately against Gram-Schmidt nearest plane in the
+  one-sided tests.
+* The cost: exact multiplication counts of both forms, n^3 + 3 n^2 against
+  2.5 n^4 - n^2 / 2 (方法: O(n^4) -> O(n^3)).
 """
-import time
-
 import numpy as np
 import pytest
 
@@ -64,22 +65,95 @@ def test_rejects_singular_basis():
         oracle.two_sided_antidiagonal(Y, RL, RR)
 
 
-@pytest.mark.slow
-def test_cost_exponents():
-    """Cubic vs quartic growth (方法: O(n^4) -> O(n^3)); fitted on small n."""
-    # best of five: the first call at each size also pays one-time costs
-    # (first touch of its intermediates, up to 680 MB at n = 96) that can
-    # exceed the work itself, and host load varies
-    def t(fn, n, reps=5):
-        Y, RL, RR = synth.two_sided_inputs(n)
-        best = 1e9
-        for _ in range(reps):
-            t0 = time.perf_counter()
-            fn(Y, RL, RR)
-            best = min(best, time.perf_counter() - t0)
-        return best
+def test_right_identity_reduces_to_one_sided():
+    """With R_R = I the metric is sum over columns of e_col^T R_L^T R_L e_col, so
+    every column of Y is rounded on its own.  Along a column the schedule takes
+    rows from last to first (i + j falls), so one-sided GPTQ sees the column
+    reversed, with H = J R_L^T R_L J."""
+    n = 13
+    Y, RL, _ = synth.two_sided_inputs(n)
+    Z = oracle.two_sided_antidiagonal(Y, RL, np.eye(n))
+    J = np.eye(n)[::-1]
+    H = J @ (RL.T @ RL) @ J
+    U = oracle.prepare(H, damp=0.0)["U"]
+    _, What, _ = oracle.column_loop(Y.T @ J, U, lambda j, Wc: np.rint(Wc[:, j]))
+    np.testing.assert_array_equal((What @ J).T, Z)
+    # the reduction is not vacuous: the feedback changes some entries
+    assert np.any(Z != np.rint(Y))
 
-    ns = [48, 64, 96]
-    tq = [t(oracle.two_sided_quartic, n) for n in ns]
-    slope_q = np.polyfit(np.log(ns), np.log(tq), 1)[0]
-    assert slope_q > 3.0   # quartic, clearly above the cubic form's 3
+
+class _Counted(np.ndarray):
+    """ndarray that counts the multiplications its ufuncs perform: one per
+    output element of multiply / divide, and inner-dimension many per output
+    element of matmul (dot products)."""
+    mults = 0
+
+    def __array_ufunc__(self, ufunc, method, *inputs, out=None, **kw):
+        plain = [x.view(np.ndarray) if isinstance(x, _Counted) else x for x in inputs]
+        if out is not None:
+            kw["out"] = tuple(o.view(np.ndarray) if isinstance(o, _Counted) else o for o in out)
+        res = getattr(ufunc, method)(*plain, **kw)
+        if method == "__call__":
+            if ufunc is np.matmul:
+                _Counted.mults += int(np.size(res)) * int(np.shape(plain[0])[-1])
+            elif ufunc in (np.multiply, np.divide):
+                _Counted.mults += int(np.size(res))
+        if out is not None:
+            return out[0] if len(out) == 1 else out
+        return res.view(_Counted) if isinstance(res, np.ndarray) else res
+
+
+class _CountingNumpy:
+    """Stand-in for the numpy module inside the two-sided oracle: arrays it
+    creates are _Counted, everything else is numpy's own."""
+
+    def __getattr__(self, name):
+        return getattr(np, name)
+
+    @staticmethod
+    def _c(a):
+        return np.asarray(a).view(_Counted)
+
+    def asarray(self, a, dtype=None):
+        return self._c(np.asarray(a, dtype=dtype))
+
+    def triu(self, a, k=0):
+        return self._c(np.triu(np.asarray(a), k))
+
+    def zeros(self, shape, dtype=float):
+        return self._c(np.zeros(shape, dtype))
+
+    def diag(self, a, k=0):
+        return self._c(np.diag(np.asarray(a), k))
+
+
+def test_cost_exponents_by_operation_count(monkeypatch):
+    """方法: the anti-diagonal schedule costs O(n^3) against the vectorized
+    (Kronecker) method's O(n^4).  The multiplications each form of the oracle
+    performs are counted exactly (a deterministic count, not a timing) at
+    n = 8, 16, 32 (quartic) and 16, 32, 64 (anti-diagonal, whose n^2 terms
+    still weigh at n = 8), and the fitted exponents are 4 and 3."""
+    from oracle import gptq2d_oracle as g2
+    monkeypatch.setattr(g2, "np", _CountingNumpy())
+    sizes = {"quartic": [8, 16, 32], "cubic": [16, 32, 64]}
+    counts = {}
+    for name, fn in (("quartic", g2.two_sided_quartic), ("cubic", g2.two_sided_antidiagonal)):
+        counts[name] = []
+        for n in sizes[name]:
+            Y, RL, RR = synth.two_sided_inputs(n)
+            _Counted.mults = 0
+            fn(Y, RL, RR)
+            counts[name].append(_Counted.mults)
+    slope = {k: np.polyfit(np.log(sizes[k]), np.log(v), 1)[0] for k, v in counts.items()}
+    print(counts, slope)
+    # quartic: the Kronecker basis (n^4 products), M vec(Y) (n^4) and the
+    # back substitution (n^2 (n^2 - 1) / 2 products): 2.5 n^4 - n^2 / 2
+    for n, c in zip(sizes["quartic"], counts["quartic"]):
+        assert c == 2 * n ** 4 + n * n * (n * n - 1) // 2
+    # anti-diagonal: entry (i, j) takes a feedback sum of n - i products and
+    # a row update of j + 1 (n^2 (n + 1) over all entries), and each
+    # anti-diagonal scales its entries' sums (2 n^2 over all): n^3 + 3 n^2
+    for n, c in zip(sizes["cubic"], counts["cubic"]):
+        assert c == n ** 3 + 3 * n ** 2
+    assert 3.95 <= slope["quartic"] <= 4.05
+    assert 2.85 <= slope["cubic"] <= 3.05
