@@ -85,15 +85,23 @@ size_t gptq_hessian_workspace(int64_t d, int64_t n_tokens, int x_dtype);
  * Then U [d x d] float32 is written: the upper triangular matrix with positive
  * diagonal and U^T U = H^{-1} (the strict lower triangle of U is set to 0).
  * It is computed as U = V^{-1} where H = V V^T with V upper triangular, which
- * is the same unique factor as chol(H^{-1}); arithmetic is fp32 (the lambda
- * shift is formed in float64).
+ * is the same unique factor as chol(H^{-1}); arithmetic is fp32 with fused
+ * multiply-adds (the lambda shift is formed in float64).  The factorization
+ * is blocked in panels of 256 columns, each run by one launch whose
+ * workgroups hand results to each other through flags in `ws`; every such
+ * wait is bounded.
  *
  * dead       [d] uint8 out, may be NULL.
- * dev_status [1] int32 out (device): 0 on success, otherwise 1 + the index
- *            (in H's numbering) of the first diagonal element found
- *            non-positive.  The elimination runs from index d-1 down to 0.
- *            U is unspecified when dev_status != 0.
- * ws         scratch of gptq_prepare_workspace(d) bytes.
+ * dev_status [1] int32 out (device): 0 on success; > 0: 1 + the index (in
+ *            H's numbering) of the first diagonal element found non-positive
+ *            (the elimination runs from index d-1 down to 0); -1: a bounded
+ *            wait between workgroups expired and the factorization did not
+ *            complete (not expected in normal operation; the environment
+ *            variable GPTQ_SYNC_SPIN_LIMIT, read once per process, sets the
+ *            number of polls, default 2^20).  U is unspecified when
+ *            dev_status != 0.
+ * ws         scratch of gptq_prepare_workspace(d) bytes (three d x d float32
+ *            matrices plus O(d) more); its contents on entry do not matter.
  * ------------------------------------------------------------------------- */
 int gptq_prepare_hinv(float* H, int64_t d, double damp, float* U, uint8_t* dead,
                       int32_t* dev_status, void* ws, size_t ws_bytes, gptq_stream stream);

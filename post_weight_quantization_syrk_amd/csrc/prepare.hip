@@ -6,51 +6,67 @@
 // and factorizing again, it is formed as U = V^{-1} with H = V V^T, V upper: in
 // the index-reversed space A = J H J (J reverses the order) this is an ordinary
 // Cholesky A = L L^T and a triangular inverse M = L^{-1}, and U = J M J.  Both
-// run blocked (64 x 64 blocks) in fp32, right-looking, per step k:
-//   diag   : L_kk = chol(A_kk) and its inverse, one workgroup;
-//   panel  : L_ik = A_ik L_kk^{-T} (i > k) and M_kj = L_kk^{-1} B_kj (j < k);
-//   update : A_ij -= L_ik L_jk^T (i >= j > k) and B_ij -= L_ik M_kj (i > k >= j),
-// where B accumulates the right-hand side of L M = I.  Steps go in groups of
-// UG: inside a group only the next block column (and block row of B) is
-// brought up to date before each step (fac_colupd_kernel, which also applies
-// the previous step's panel), and after the group the trailing part receives
-// the group's panels in two pieces: the band the next group's steps read
-// (fac_update_kernel, whose workgroup on the next diagonal block factorizes it
-// in the same launch), and the rest through extra workgroups of the next
-// group's column-update launches, which by themselves leave most of the chip
-// idle.
-// Panel and update tiles are fp32 MFMA products (v_mfma_f32_32x32x2f32).
+// run in fp32 with IEEE fused multiply-adds (the fp32 matrix cores round like a
+// chain of FMAs):
+//   Cholesky, two-level and right-looking.  Panels of PW = 256 columns; each
+//     is factorized by one persistent launch (chol_panel_kernel) in four
+//     64-column steps: the 64 x 64 diagonal block is factorized and inverted
+//     by one workgroup, every row block below multiplies its block by that
+//     inverse (L_rj = A_rj L_jj^{-T}) and updates its later panel columns,
+//     workgroups handing results to each other through release/acquire flags
+//     with bounded waits.  Each workgroup keeps its row block's panel columns
+//     in registers for the whole panel.  After the panel, the trailing matrix
+//     receives the panel at once (chol_syrk_kernel, K = 256).
+//   Inverse, by recursive doubling: with the diagonal blocks' inverses from the
+//     panels, blocks of size s pair up into blocks of 2s,
+//       inv([L11 0; L21 L22]) = [X11 0; -X22 L21 X11  X22],
+//     two matrix-product launches per level (inv_t_kernel: T = L21 X11,
+//     inv_x_kernel: X21 = -X22 T), log2(d / 64) levels.
+// Every product is an fp32 MFMA tile (v_mfma_f32_32x32x2f32).  This ordering
+// keeps the rounding error of a textbook blocked factorization: U comes out
+// within a few times sqrt(d) u sqrt(kappa(H)) of the exact factor.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_f32.h"
 
 #include <algorithm>
+#include <cstdlib>
 
 namespace gptq {
 
 namespace {
 
 constexpr int NB = 64;
-constexpr int UG = 4;   // steps per delayed trailing update
+constexpr int NJ = 4;                        // 64-column steps per panel
+constexpr int PW = NB * NJ;                  // panel width
+constexpr int FLAGS_PER_PANEL = NJ + NJ * NJ;  // diagonal-block flags, then block-column flags
+constexpr int SYNC_TIMEOUT = -1;             // dev_status when a bounded wait expires
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct PrepWs {
   float* A;      // [d x d] reversed damped H, then L (lower)
-  float* M;      // [d x d] right-hand side / L^{-1} (lower)
-  float* Dinv[2];  // [NB x NB] inverse of the diagonal block of step k, in Dinv[k % 2]
+  float* M;      // [d x d] L^{-1} (lower)
+  float* T;      // [d x d] the inverse's products T = L21 X11 (lower blocks)
+  float* Dinv;   // [nb][NB x NB] inverses of the diagonal blocks
+  int* flags;    // [panels][FLAGS_PER_PANEL]
   double* scal;  // [0] = lambda
 };
+
+inline int64_t n_panels(int64_t d) { return (d + PW - 1) / PW; }
 
 PrepWs carve(void* ws, int64_t d) {
   char* p = (char*)ws;
   PrepWs w;
   const size_t mat = align256((size_t)d * d * sizeof(float));
+  const size_t dinv = align256((size_t)((d + NB - 1) / NB) * NB * NB * sizeof(float));
+  const size_t flg = align256((size_t)n_panels(d) * FLAGS_PER_PANEL * sizeof(int));
   w.A = (float*)p;
   w.M = (float*)(p + mat);
-  w.Dinv[0] = (float*)(p + 2 * mat);
-  w.Dinv[1] = (float*)(p + 2 * mat + align256(NB * NB * sizeof(float)));
-  w.scal = (double*)(p + 2 * mat + 2 * align256(NB * NB * sizeof(float)));
+  w.T = (float*)(p + 2 * mat);
+  w.Dinv = (float*)(p + 3 * mat);
+  w.flags = (int*)(p + 3 * mat + dinv);
+  w.scal = (double*)(p + 3 * mat + dinv + flg);
   return w;
 }
 
@@ -88,11 +104,10 @@ __global__ __launch_bounds__(1024) void prep_stats_kernel(const float* __restric
 
 // Mirror the lower triangle of H into the upper one, damp the diagonal
 // (lambda added in float64, stored rounded to fp32), and build A = J H J
-// (lower triangle) and zero the lower triangle of M.
+// (lower triangle).
 __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, int d,
                                                          const double* __restrict__ scal,
-                                                         float* __restrict__ A,
-                                                         float* __restrict__ M) {
+                                                         float* __restrict__ A) {
   __shared__ float t[32][33];
   int ti, tj;
   tri_coords(blockIdx.x, ti, tj);
@@ -117,7 +132,6 @@ __global__ __launch_bounds__(256) void prep_build_kernel(float* __restrict__ H, 
       H[(int64_t)j * d + i] = v;
       A[ar * d + ac] = v;
     }
-    M[ar * d + ac] = 0.0f;
   }
 }
 
@@ -409,344 +423,311 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
   }
 }
 
-__global__ __launch_bounds__(256) void fac_diag_kernel(float* __restrict__ A,
-                                                       float* __restrict__ M,
-                                                       float* __restrict__ Dinv, int d, int k,
-                                                       int32_t* status) {
-  if (*status != 0) return;
-  __shared__ DiagLds L;
-  diag_load(L, A, d, k);
+
+// ---- synchronisation between the workgroups of one panel launch ----------
+// Flags live in the workspace and are cleared before the panels start.  A
+// producer writes its results, makes them visible device-wide (release fence
+// by every thread, then a release store of the flag); a consumer's thread 0
+// polls the flag with acquire loads, every thread then takes an acquire fence
+// before reading the results.  Every wait is bounded: it also stops when the
+// factorization has failed (dev_status set by another workgroup) or after
+// `spin` polls, which sets dev_status to SYNC_TIMEOUT; either way the
+// workgroup leaves, so the launch always drains.
+__global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int64_t n) {
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+    p[e] = 0;
+}
+
+__device__ __forceinline__ void publish(int* flag) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   __syncthreads();
-  diag_factor(L, A, M, Dinv, d, k, status);
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
+__device__ __forceinline__ bool wait_flag(const int* flag, int32_t* status, int64_t spin,
+                                          int* ok_lds) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    for (int64_t it = 0;; ++it) {
+      if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) != 0) break;
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+        ok = 0;
+        break;
+      }
+      if (it >= spin) {
+        atomicCAS((int*)status, 0, SYNC_TIMEOUT);
+        ok = 0;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    if (ok && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) ok = 0;
+    *ok_lds = ok;
+  }
+  __syncthreads();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  const bool ok = *ok_lds != 0;
+  __syncthreads();  // everyone has read ok_lds before it is written again
+  return ok;
+}
+
+// One panel of the Cholesky factorization: columns [c0, c0 + pw), pw =
+// min(PW, d - c0), rows c0 .. d-1, everything left of c0 already applied.
+// Workgroup r owns row block r (rows c0 + 64 r ..), and holds its blocks of
+// the panel's column blocks j = 0 .. min(r, nj - 1) in accumulator registers
+// (one 32 x 32 MFMA tile per wave and block).  Step j:
+//   workgroup j      : factorizes and inverts its diagonal block (into A, M
+//                      and Dinv), publishes flag diag[j] and is done;
+//   workgroups r > j : wait for diag[j]; L_rj = A_rj Dinv_j^T; the panel's
+//                      row blocks (r < nj) publish L_rj (flag col[j][r]);
+//                      then A_{r,jj} -= L_rj L_{jj,j}^T for j < jj <= min(r,
+//                      nj - 1), waiting for col[j][jj] (jj != r); the
+//                      product is summed from zero and subtracted once.
+// Every workgroup waits only on workgroups 0 .. nj-1, which never wait on a
+// later one, so the launch completes whatever the residency.
 using TileT = MfmaTile<NB, NB, NB, true>;   // C = P Q with Q given transposed
-using TileN = MfmaTile<NB, NB, NB, false>;  // C = P Q with Q row-major
-constexpr size_t TILE_LDS = (TileT::lds_floats > TileN::lds_floats ? TileT::lds_floats
-                                                                     : TileN::lds_floats);
+static_assert(TileT::FM == 1 && TileT::FN == 1, "one MFMA tile per wave and block");
 
-template <class Tile, bool SUB>
-__device__ __forceinline__ void tile_store(float* C, int64_t ld, int rows, int cols,
-                                           const f32x16 (&acc)[Tile::FM][Tile::FN]) {
-  Tile::template store<SUB>(C, ld, rows, cols, acc);
-}
-
-// Panel: L_ik = A_ik Dinv^T for row blocks i > k; M_kj = Dinv B_kj for column blocks j < k.
-__global__ __launch_bounds__(256) void fac_panel_kernel(float* __restrict__ A,
-                                                        float* __restrict__ M,
-                                                        const float* __restrict__ Dinv, int d,
-                                                        int k, int nrow, const int32_t* status) {
-  if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[TILE_LDS];
-  const int k0 = k * NB, kb = min(NB, d - k0);
-  const int wg = blockIdx.x;
-  if (wg < nrow) {
-    const int i0 = (k + 1 + wg) * NB, ib = min(NB, d - i0);
-    float* Aik = A + (int64_t)i0 * d + k0;
-    f32x16 acc[TileT::FM][TileT::FN];
-    TileT::zero(acc);
-    TileT::load_p(lds, Aik, d, ib, kb);
-    TileT::load_q(lds, Dinv, NB, NB, NB);  // Q^T = Dinv
-    __syncthreads();
-    TileT::mma(lds, acc);
-    tile_store<TileT, false>(Aik, d, ib, kb, acc);
-  } else {
-    const int j0 = (wg - nrow) * NB;  // full block, j < k
-    float* Mkj = M + (int64_t)k0 * d + j0;
-    f32x16 acc[TileN::FM][TileN::FN];
-    TileN::zero(acc);
-    TileN::load_p(lds, Dinv, NB, NB, NB);
-    TileN::load_q(lds, Mkj, d, kb, NB);
-    __syncthreads();
-    TileN::mma(lds, acc);
-    __syncthreads();
-    tile_store<TileN, false>(Mkj, d, kb, NB, acc);
-  }
-}
-
-// After a group of steps [mlo, mhi) (delayed, grouped updates: the trailing
-// matrix is read and written once per group of steps instead of once per
-// step), both factorizations receive the group's panels:
-//   L tiles  A_ij -= sum_m L_im L_jm^T   (i >= j >= mhi)
-//   M tiles  B_ij -= sum_m L_im M_mj     (i >= mhi, j < mhi; only m >= j
-//                                         contributes: M is lower)
-// Each step m is one K = 64 chunk through LDS, accumulated in registers.
-// One output tile (block bi, bj) per call; with diag (tile (mhi, mhi) only)
-// the updated block goes from its accumulators straight into the diagonal
-// factorization's LDS copies and is factorized into Dinv instead of stored.
-__device__ __forceinline__ void update_tile(float* __restrict__ A, float* __restrict__ M,
-                                            float* __restrict__ Dinv, float* lds, int d,
-                                            int mlo, int mhi, bool ltile, int bi, int bj,
-                                            bool diag, int32_t* status) {
-  const int i0 = bi * NB, j0 = bj * NB;
-  const int ib = min(NB, d - i0), jb = min(NB, d - j0);
-  // The output tile is loaded into the accumulators and the products
-  // accumulate onto it with P negated on its way into LDS; step m+1's
-  // operands are loaded while step m multiplies.
-  if (ltile) {
-    float* C = A + (int64_t)i0 * d + j0;
-    f32x16 acc[TileT::FM][TileT::FN];
-    TileT::set_each(acc, [&](int row, int col) {
-      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < jb ? col : jb - 1)];
-    });
-    TileT::PQRegs v;
-    auto fetch = [&](int m) __attribute__((always_inline)) {
-      const int m0 = m * NB, mb = min(NB, d - m0);
-      TileT::fetch_pq(v, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
-                      A + (int64_t)j0 * d + m0, d, jb, mb);     // Q^T = L_jm
-    };
-    fetch(mlo);
-    for (int m = mlo; m < mhi; ++m) {
-      const int mb = min(NB, d - m * NB);
-      if (m > mlo) __syncthreads();
-      TileT::stage_pq<true>(lds, v, ib, mb, jb, mb);
-      __syncthreads();
-      if (m + 1 < mhi) fetch(m + 1);
-      TileT::mma(lds, acc);
-    }
-    if (diag) {
-      DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
-      __syncthreads();  // every wave is done with the product's LDS operands
-      TileT::for_each(acc, [&](int row, int col, float val) {
-        L.tile[row][col] = diag_entry(row, col, ib, val);
-      });
-      for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
-      __syncthreads();
-      diag_factor(L, A, M, Dinv, d, bi, status);
-      return;
-    }
-    tile_store<TileT, false>(C, d, ib, jb, acc);
-  } else {
-    const int ms = max(mlo, bj);
-    if (ms >= mhi) return;
-    float* C = M + (int64_t)i0 * d + j0;
-    f32x16 acc[TileN::FM][TileN::FN];
-    TileN::set_each(acc, [&](int row, int col) {
-      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < jb ? col : jb - 1)];
-    });
-    TileN::PQRegs v;
-    auto fetch = [&](int m) __attribute__((always_inline)) {
-      const int m0 = m * NB, mb = min(NB, d - m0);
-      TileN::fetch_pq(v, A + (int64_t)i0 * d + m0, d, ib, mb,   // P = L_im
-                      M + (int64_t)m0 * d + j0, d, mb, jb);     // Q = M_mj
-    };
-    fetch(ms);
-    for (int m = ms; m < mhi; ++m) {
-      const int mb = min(NB, d - m * NB);
-      if (m > ms) __syncthreads();
-      TileN::stage_pq<true>(lds, v, ib, mb, mb, jb);
-      __syncthreads();
-      if (m + 1 < mhi) fetch(m + 1);
-      TileN::mma(lds, acc);
-    }
-    tile_store<TileN, false>(C, d, ib, jb, acc);
-  }
-}
-
-// The tiles a group's update touches split in two.  The band -- L block
-// columns [mhi, mhi + UG) and B block rows [mhi, mhi + UG), what the next
-// group's steps read -- is updated right after the group (fac_update_kernel).
-// The rest -- L block columns and B block rows from mhi + UG on -- is read by
-// nothing until the next group's own update, and is updated meanwhile by
-// extra workgroups of the next group's column-update launches, on the compute
-// units those latency-bound launches leave idle.  The two sets are disjoint
-// from each other and from everything the next group's column updates and
-// panel read or write.
-__host__ __device__ inline int band_ltiles(int nb, int c0, int c1) {
-  return (c1 - c0) * nb - (c0 + c1 - 1) * (c1 - c0) / 2;
-}
-__host__ __device__ inline int band_tiles(int nb, int mhi) {
-  const int c1 = min(nb, mhi + UG);
-  return band_ltiles(nb, mhi, c1) + (c1 - mhi) * mhi;
-}
-__host__ __device__ inline int rest_tiles(int nb, int mhi) {
-  const int T = nb - (mhi + UG);
-  return T > 0 ? T * (T + 1) / 2 + T * mhi : 0;
-}
-
-// Band tile t: L tiles column by column from (mhi, mhi) down, then the B
-// tiles row by row.  Workgroup 0 (tile (mhi, mhi)) also factorizes the next
-// diagonal block into Dinv: it touches only block (mhi, mhi) of A and M and
-// Dinv, which no other tile of this launch reads.
-__global__ __launch_bounds__(256) void fac_update_kernel(float* __restrict__ A,
-                                                         float* __restrict__ M,
-                                                         float* __restrict__ Dinv, int d, int nb,
-                                                         int mlo, int mhi, int32_t* status) {
-  if (*status != 0) return;
-  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
-  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
-  const int c1 = min(nb, mhi + UG);
-  int t = blockIdx.x;
-  const int nl = band_ltiles(nb, mhi, c1);
-  if (t < nl) {
-    int bj = mhi;
-    while (t >= nb - bj) {
-      t -= nb - bj;
-      ++bj;
-    }
-    update_tile(A, M, Dinv, lds, d, mlo, mhi, true, bj + t, bj, blockIdx.x == 0, status);
-  } else {
-    t -= nl;
-    update_tile(A, M, Dinv, lds, d, mlo, mhi, false, mhi + t / mhi, t % mhi, false, status);
-  }
-}
-
-// Rest tile t of the group [mhi - UG, mhi): the L triangle from block mhi + UG
-// row by row, then the B tiles row by row.
-__device__ __forceinline__ void rest_tile(float* __restrict__ A, float* __restrict__ M,
-                                          float* lds, int d, int nb, int mhi, int t,
-                                          int32_t* status) {
-  const int c0 = mhi + UG, T = nb - c0, ta = T * (T + 1) / 2;
-  if (t < ta) {
-    int ii, jj;
-    tri_coords(t, ii, jj);
-    update_tile(A, M, nullptr, lds, d, mhi - UG, mhi, true, c0 + ii, c0 + jj, false, status);
-  } else {
-    t -= ta;
-    update_tile(A, M, nullptr, lds, d, mhi - UG, mhi, false, c0 + t / mhi, t % mhi, false,
-                status);
-  }
-}
-
-// Part 1 of step kc (g0 < kc < group end) with step p = kc - 1's panel folded
-// in, so no panel launch sits between the two diagonal factorizations:
-//   L tile (i, kc), i >= kc:  P_i = A_ip Dinv_p^T (stored: the panel block
-//     L_ip) and P_k = A_kc,p Dinv_p^T (recomputed by every workgroup), then
-//     A_i,kc -= sum_{m in [g0, p)} L_im L_kc,m^T + P_i P_k^T;
-//   B tile (kc, j), j < kc:   for j < p, M_pj = Dinv_p B_pj (stored: the
-//     panel's block of L^{-1}); M_pp = Dinv_p; then
-//     B_kc,j -= sum_{m in [max(g0, j), p)} L_kc,m M_mj + P_k M_pj.
-// The output tile is preloaded into the accumulators and the products
-// accumulate onto it with P negated.  Workgroup 0 (tile (kc, kc)) then
-// factorizes the diagonal block, as in fac_update_kernel, into Dinv_out (the
-// other buffer: the others read Dinv_p throughout).  Block p is never the
-// last block, so it is a full one.
-__global__ __launch_bounds__(256, 2) void fac_colupd_kernel(float* __restrict__ A,
-                                                         float* __restrict__ M,
-                                                         const float* __restrict__ Dinv,
-                                                         float* __restrict__ Dinv_out, int d,
-                                                         int nb, int g0, int kc, int rest_lo,
-                                                         int32_t* status) {
-  if (*status != 0) return;
-  constexpr size_t LDS_FLOATS = TILE_LDS > DIAG_LDS_FLOATS ? TILE_LDS : DIAG_LDS_FLOATS;
-  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
-  if ((int)blockIdx.x >= nb) {  // the previous group's rest tiles
-    rest_tile(A, M, lds, d, nb, g0, rest_lo + (int)blockIdx.x - nb, status);
-    return;
-  }
-  const int p = kc - 1, p0 = p * NB, kc0 = kc * NB;
-  const int kcb = min(NB, d - kc0);
-  const int wg = blockIdx.x, T = nb - kc;
-  const float* Akp = A + (int64_t)kc0 * d + p0;
-  // acc = (rows x 64 block at src) * Dinv_p^T
-  auto panel_t = [&](f32x16 (&acc)[TileT::FM][TileT::FN], const float* src, int rows)
-      __attribute__((always_inline)) {
-    TileT::zero(acc);
-    TileT::load_p(lds, src, d, rows, NB);
-    TileT::load_q(lds, Dinv, NB, NB, NB);  // Q^T = Dinv_p
-    __syncthreads();
-    TileT::mma(lds, acc);
-    __syncthreads();  // LDS free again
-  };
-  if (wg < T) {
-    const int i = kc + wg, i0 = i * NB, ib = min(NB, d - i0);
-    f32x16 pi[TileT::FM][TileT::FN], pk[TileT::FM][TileT::FN];
-    panel_t(pi, A + (int64_t)i0 * d + p0, ib);
-    if (wg == 0) {
+template <class F>
+__device__ __forceinline__ void acc_each(const f32x16& a, F&& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pk[0][0][r] = pi[0][0][r];
-    } else {
-      panel_t(pk, Akp, kcb);
-    }
-    // L_ip, for the rows below kc (row kc's is used only here, and every
-    // workgroup reads row kc's A_kc,p, so it stays as it is)
-    if (wg != 0) tile_store<TileT, false>(A + (int64_t)i0 * d + p0, d, ib, NB, pi);
-    float* C = A + (int64_t)i0 * d + kc0;
-    f32x16 acc[TileT::FM][TileT::FN];
-    TileT::set_each(acc, [&](int row, int col) {
-      return C[(int64_t)(row < ib ? row : ib - 1) * d + (col < kcb ? col : kcb - 1)];
+  for (int q = 0; q < 16; ++q)
+    f(wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), wn * 32 + (lane & 31), q);
+}
+
+// Stage a register block as the P operand (rows x cols valid, zero outside),
+// negated when NEG.
+template <bool NEG>
+__device__ __forceinline__ void stage_p_regs(float* lds, const f32x16& a, int rows, int cols) {
+  acc_each(a, [&](int row, int col, int q) {
+    const float x = a[q];
+    lds[row * TileT::PP + col] = (row < rows && col < cols) ? (NEG ? -x : x) : 0.0f;
+  });
+}
+// Stage a register block as the Q^T operand (rows = n, cols = k valid).
+__device__ __forceinline__ void stage_q_regs(float* lds, const f32x16& a, int rows, int cols) {
+  acc_each(a, [&](int row, int col, int q) {
+    lds[TileT::lds_q_offset + row * TileT::QPITCH + col] =
+        (row < rows && col < cols) ? a[q] : 0.0f;
+  });
+}
+
+// Blocks handed from one workgroup to another inside a launch are written and
+// read with system-coherent accesses, which bypass the per-XCD L2 caches:
+// with ordinary accesses, release/acquire at device scope was measured to let
+// a reader on another XCD see stale data (wrong factors, varying from call to
+// call), and with these accesses the results are bit-reproducible.
+__device__ __forceinline__ void xstore(float* p, float v) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float xload(const float* p) {
+  return __uint_as_float(
+      __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
+}
+// Q^T operand (rows x cols valid, zero outside) from another workgroup's block.
+__device__ __forceinline__ void load_q_xchg(float* lds, const float* src, int64_t ld, int rows,
+                                            int cols) {
+  float v[NB * NB / 256];
+#pragma unroll
+  for (int u = 0; u < NB * NB / 256; ++u) {
+    const int e = u * 256 + threadIdx.x, r = e / NB, c = e % NB;
+    v[u] = xload(src + (int64_t)min(r, rows - 1) * ld + min(c, cols - 1));
+  }
+#pragma unroll
+  for (int u = 0; u < NB * NB / 256; ++u) {
+    const int e = u * 256 + threadIdx.x, r = e / NB, c = e % NB;
+    lds[TileT::lds_q_offset + r * TileT::QPITCH + c] = (r < rows && c < cols) ? v[u] : 0.0f;
+  }
+}
+
+__device__ __forceinline__ void mma1(const float* lds, f32x16& acc) {
+  TileT::mma(lds, *reinterpret_cast<f32x16(*)[1][1]>(&acc));
+}
+
+__global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
+                                                         float* __restrict__ M,
+                                                         float* __restrict__ Dinv,
+                                                         int* __restrict__ flags, int d, int c0,
+                                                         int32_t* status, int64_t spin) {
+  if (*status != 0) return;
+  constexpr size_t LDS_FLOATS = TileT::lds_floats > DIAG_LDS_FLOATS ? TileT::lds_floats
+                                                                      : DIAG_LDS_FLOATS;
+  __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
+  __shared__ int ok_lds;
+  const int r = blockIdx.x;
+  const int pw = min(PW, d - c0), nj = (pw + NB - 1) / NB;
+  const int i0 = c0 + NB * r, ib = min(NB, d - i0);
+  int* fdiag = flags + (int64_t)(c0 / PW) * FLAGS_PER_PANEL;
+  int* fcol = fdiag + NJ;
+  const int jmax = min(r, nj - 1);
+  // this row block's panel blocks (unconditional loads from clamped
+  // addresses; blocks past jmax are never used)
+  f32x16 acc[NJ];
+  StaticFor<0, NJ>::run([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const int k0 = min(c0 + NB * j, d - 1), kb = max(1, min(NB, d - k0));
+    acc_each(acc[j], [&](int row, int col, int q) {
+      acc[j][q] = A[(int64_t)(i0 + min(row, ib - 1)) * d + k0 + min(col, kb - 1)];
     });
-    TileT::PQRegs v;
-    auto fetch = [&](int m) __attribute__((always_inline)) {
-      TileT::fetch_pq(v, A + (int64_t)i0 * d + m * NB, d, ib, NB,   // P = L_im
-                      A + (int64_t)kc0 * d + m * NB, d, kcb, NB);   // Q^T = L_kc,m
-    };
-    if (g0 < p) fetch(g0);
-    for (int m = g0; m < p; ++m) {
-      if (m > g0) __syncthreads();
-      TileT::stage_pq<true>(lds, v, ib, NB, kcb, NB);
-      __syncthreads();
-      if (m + 1 < p) fetch(m + 1);
-      TileT::mma(lds, acc);
-    }
-    // step p from registers: P = -P_i, Q^T = P_k
-    __syncthreads();
-    TileT::for_each(pi, [&](int row, int col, float x) { lds[row * TileT::PP + col] = -x; });
-    TileT::for_each(pk, [&](int row, int col, float x) {
-      lds[TileT::lds_q_offset + row * TileT::QPITCH + col] = x;
-    });
-    __syncthreads();
-    TileT::mma(lds, acc);
-    if (wg == 0) {
+  });
+  bool done = false;
+  StaticFor<0, NJ>::run([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    if (done || j > jmax) return;
+    const int k0 = c0 + NB * j, kb = min(NB, d - k0), kg = k0 / NB;
+    if (j == r) {
+      // the diagonal block, brought up to date in registers, straight into the
+      // factorization's LDS copy
       DiagLds& L = *reinterpret_cast<DiagLds*>(lds);
-      __syncthreads();  // every wave is done with the product's LDS operands
-      TileT::for_each(acc, [&](int row, int col, float val) {
-        L.tile[row][col] = diag_entry(row, col, ib, val);
+      __syncthreads();
+      acc_each(acc[j], [&](int row, int col, int q) {
+        L.tile[row][col] = diag_entry(row, col, kb, acc[j][q]);
       });
       for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
       __syncthreads();
-      diag_factor(L, A, M, Dinv_out, d, kc, status);
+      diag_factor(L, A, M, Dinv + (size_t)kg * NB * NB, d, kg, status);
+      // the inverse again, for the other workgroups, from its LDS copy
+      for (int e = threadIdx.x; e < NB * NB; e += 256)
+        xstore(Dinv + (size_t)kg * NB * NB + e, L.mtile[e / NB][e % NB]);
+      publish(fdiag + j);
+      done = true;
       return;
     }
-    tile_store<TileT, false>(C, d, ib, kcb, acc);
-  } else {
-    const int j = wg - T, j0 = j * NB;  // full block, j < kc
-    f32x16 mpj[TileN::FM][TileN::FN];
-    if (j < p) {
-      TileN::zero(mpj);
-      TileN::load_p(lds, Dinv, NB, NB, NB);
-      TileN::load_q(lds, M + (int64_t)p0 * d + j0, d, NB, NB);  // B_pj
-      __syncthreads();
-      TileN::mma(lds, mpj);
-      __syncthreads();
-      tile_store<TileN, false>(M + (int64_t)p0 * d + j0, d, NB, NB, mpj);  // M_pj
+    if (!wait_flag(fdiag + j, status, spin, &ok_lds)) {
+      done = true;
+      return;
     }
-    f32x16 pk[TileT::FM][TileT::FN];
-    panel_t(pk, Akp, kcb);
-    float* C = M + (int64_t)kc0 * d + j0;
-    f32x16 acc[TileN::FM][TileN::FN];
-    TileN::set_each(acc, [&](int row, int col) {
-      return C[(int64_t)(row < kcb ? row : kcb - 1) * d + col];
+    // L_rj = A_rj Dinv_j^T
+    stage_p_regs<false>(lds, acc[j], ib, kb);
+    load_q_xchg(lds, Dinv + (size_t)kg * NB * NB, NB, NB, NB);
+    __syncthreads();
+    TileT::zero(*reinterpret_cast<f32x16(*)[1][1]>(&acc[j]));
+    mma1(lds, acc[j]);
+    __syncthreads();
+    float* Arj = A + (int64_t)i0 * d + k0;
+    acc_each(acc[j], [&](int row, int col, int q) {
+      if (row < ib && col < kb) {
+        if (r < nj)
+          xstore(Arj + (int64_t)row * d + col, acc[j][q]);
+        else
+          Arj[(int64_t)row * d + col] = acc[j][q];
+      }
     });
-    const int ms = max(g0, j);
-    TileN::PQRegs v;
-    auto fetch = [&](int m) __attribute__((always_inline)) {
-      TileN::fetch_pq(v, A + (int64_t)kc0 * d + m * NB, d, kcb, NB,   // P = L_kc,m
-                      M + (int64_t)m * NB * d + j0, d, NB, NB);       // Q = M_mj
-    };
-    if (ms < p) fetch(ms);
-    for (int m = ms; m < p; ++m) {
-      if (m > ms) __syncthreads();
-      TileN::stage_pq<true>(lds, v, kcb, NB, NB, NB);
+    if (r < nj) publish(fcol + j * NJ + r);
+    // later panel columns of this row block: A_{r,jj} -= L_rj L_{jj,j}^T
+    StaticFor<j + 1, NJ>::run([&](auto JJ) {
+      constexpr int jj = decltype(JJ)::value;
+      if (done || jj > jmax) return;
+      const int kk0 = c0 + NB * jj, kkb = min(NB, d - kk0);
+      if (jj != r) {
+        if (!wait_flag(fcol + j * NJ + jj, status, spin, &ok_lds)) {
+          done = true;
+          return;
+        }
+        load_q_xchg(lds, A + (int64_t)kk0 * d + k0, d, kkb, kb);    // Q^T = L_{jj,j}
+      } else {
+        stage_q_regs(lds, acc[j], ib, kb);                          // Q^T = L_rj itself
+      }
+      stage_p_regs<false>(lds, acc[j], ib, kb);
       __syncthreads();
-      if (m + 1 < p) fetch(m + 1);
-      TileN::mma(lds, acc);
-    }
-    // step p: P = -P_k, Q = M_pj (Dinv_p itself when j = p)
+      f32x16 prod;
+      TileT::zero(*reinterpret_cast<f32x16(*)[1][1]>(&prod));
+      mma1(lds, prod);
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[jj][q] -= prod[q];
+    });
+  });
+}
+
+// Trailing update after a panel: A[c1:, c1:] (lower tiles) -= P P^T with
+// P = L[c1:, c0:c1] (K = c1 - c0 <= 256), 128 x 128 tiles, K in chunks of 32;
+// the next chunk's operands are loaded while the current one multiplies.  The
+// products are summed from zero and subtracted from A once: summed onto a
+// preloaded A, every one of the K roundings would be at A's magnitude, which
+// on the large diagonal entries grows the factor's error like sqrt(d) u |A|.
+// Diagonal tiles are computed whole (their upper halves land in A's unused
+// upper triangle).
+using TileS = MfmaTile<128, 128, 32, true>;
+
+__global__ __launch_bounds__(256) void chol_syrk_kernel(float* __restrict__ A, int d, int c0,
+                                                        int c1, const int32_t* status) {
+  if (*status != 0) return;
+  __shared__ __attribute__((aligned(16))) float lds[TileS::lds_floats];
+  int ti, tj;
+  tri_coords(blockIdx.x, ti, tj);
+  const int i0 = c1 + 128 * ti, j0 = c1 + 128 * tj;
+  const int ib = min(128, d - i0), jb = min(128, d - j0);
+  const int kw = c1 - c0;
+  float* C = A + (int64_t)i0 * d + j0;
+  f32x16 acc[TileS::FM][TileS::FN];
+  TileS::zero(acc);
+  TileS::PQRegs v;
+  auto fetch = [&](int kc) __attribute__((always_inline)) {
+    const int kn = min(32, kw - kc);
+    TileS::fetch_pq(v, A + (int64_t)i0 * d + c0 + kc, d, ib, kn,
+                    A + (int64_t)j0 * d + c0 + kc, d, jb, kn);
+  };
+  fetch(0);
+  for (int kc = 0; kc < kw; kc += 32) {
+    const int kn = min(32, kw - kc);
+    if (kc > 0) __syncthreads();
+    TileS::stage_pq<false>(lds, v, ib, kn, jb, kn);
     __syncthreads();
-    TileT::for_each(pk, [&](int row, int col, float x) { lds[row * TileN::PP + col] = -x; });
-    if (j < p) {
-      TileN::for_each(mpj, [&](int row, int col, float x) {
-        lds[TileN::lds_q_offset + row * TileN::QPITCH + col] = x;
-      });
-    } else {
-      for (int e = threadIdx.x; e < NB * NB; e += 256)
-        lds[TileN::lds_q_offset + (e / NB) * TileN::QPITCH + e % NB] = Dinv[e];
-    }
-    __syncthreads();
-    TileN::mma(lds, acc);
-    tile_store<TileN, false>(C, d, kcb, NB, acc);
+    if (kc + 32 < kw) fetch(kc + 32);
+    TileS::mma(lds, acc);
   }
+  TileS::store<true>(C, d, ib, jb, acc);
+}
+
+// ---- the inverse: recursive doubling ------------------------------------
+// Level s (a power of two times 64): pairs (a, b = a + s, e = min(b + s, d)),
+// a = 0, 2s, 4s, ..., b < d.  Tile (rt, ct) of a pair covers rows
+// b + 64 rt .. and columns a + 64 ct ..; (s / 64)^2 tiles per pair.
+//   inv_t_kernel: T[b:e, a:b] = L[b:e, a:b] M[a:b, a:b]   (M lower: m >= ct)
+//   inv_x_kernel: M[b:e, a:b] = -M[b:e, b:e] T[b:e, a:b]  (M lower: m <= rt)
+using TileN = MfmaTile<NB, NB, NB, false>;  // C = P Q with Q row-major
+
+template <bool XSTEP>
+__global__ __launch_bounds__(256) void inv_level_kernel(const float* __restrict__ L,
+                                                        float* __restrict__ M,
+                                                        float* __restrict__ T, int d, int s,
+                                                        const int32_t* status) {
+  if (*status != 0) return;
+  __shared__ __attribute__((aligned(16))) float lds[TileN::lds_floats];
+  const int sb = s / NB;  // blocks per half
+  const int t = blockIdx.x;
+  const int p = t / (sb * sb), rem = t % (sb * sb), rt = rem / sb, ct = rem % sb;
+  const int a = 2 * s * p, b = a + s;
+  const int i0 = b + NB * rt, j0 = a + NB * ct;
+  if (i0 >= d) return;
+  const int ib = min(NB, d - i0);
+  // K range, in blocks: T step m = ct .. sb-1 over L[i0, a + 64 m] M[a + 64 m, j0];
+  // X step m = 0 .. rt over M[i0, b + 64 m] T[b + 64 m, j0]
+  const int m_lo = XSTEP ? 0 : ct, m_hi = XSTEP ? rt : sb - 1;
+  const float* Pb = XSTEP ? M + (int64_t)i0 * d + b : L + (int64_t)i0 * d + a;
+  const float* Qb = XSTEP ? T + (int64_t)b * d + j0 : M + (int64_t)a * d + j0;
+  const int qbase = XSTEP ? b : a;
+  f32x16 acc[TileN::FM][TileN::FN];
+  TileN::zero(acc);
+  TileN::PQRegs v;
+  auto fetch = [&](int m) __attribute__((always_inline)) {
+    const int mb = min(NB, d - (qbase + NB * m));
+    TileN::fetch_pq(v, Pb + NB * m, d, ib, mb, Qb + (int64_t)NB * m * d, d, mb, NB);
+  };
+  fetch(m_lo);
+  for (int m = m_lo; m <= m_hi; ++m) {
+    const int mb = min(NB, d - (qbase + NB * m));
+    if (m > m_lo) __syncthreads();
+    TileN::stage_pq<XSTEP>(lds, v, ib, mb, mb, NB);
+    __syncthreads();
+    if (m + 1 <= m_hi) fetch(m + 1);
+    TileN::mma(lds, acc);
+  }
+  float* C = (XSTEP ? M : T) + (int64_t)i0 * d + j0;
+  TileN::store<false>(C, d, ib, NB, acc);
 }
 
 // U[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -760,10 +741,23 @@ __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ 
   }
 }
 
+
+// Polls of a bounded wait before it gives up (GPTQ_SYNC_SPIN_LIMIT overrides;
+// a tiny value forces the timeout path, for tests of it).
+int64_t spin_limit() {
+  static const int64_t v = [] {
+    const char* e = std::getenv("GPTQ_SYNC_SPIN_LIMIT");
+    return e ? std::max<int64_t>(0, std::atoll(e)) : ((int64_t)1 << 20);
+  }();
+  return v;
+}
+
 }  // namespace
 
 size_t prepare_workspace(int64_t d) {
-  return 2 * align256((size_t)d * d * sizeof(float)) + 2 * align256(NB * NB * sizeof(float)) + 256;
+  const size_t mat = align256((size_t)d * d * sizeof(float));
+  return 3 * mat + align256((size_t)((d + NB - 1) / NB) * NB * NB * sizeof(float)) +
+         align256((size_t)n_panels(d) * FLAGS_PER_PANEL * sizeof(int)) + 256;
 }
 
 hipError_t prepare_launch(float* H, int64_t d64, double damp, float* U, uint8_t* dead,
@@ -779,49 +773,38 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
                      dev_status);
   const int nt32 = (int)ceil_div(d, 32);
   hipLaunchKernelGGL(prep_build_kernel, dim3(nt32 * (nt32 + 1) / 2), dim3(256), 0, stream, H, d,
-                     (const double*)w.scal, w.A, w.M);
+                     (const double*)w.scal, w.A);
   if (perm)
     hipLaunchKernelGGL(prep_perm_kernel,
                        dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 1024)), dim3(256), 0,
                        stream, (const float*)H, d, perm, w.A);
+  const int64_t nflags = n_panels(d) * FLAGS_PER_PANEL;
+  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)ceil_div(nflags, 256)), dim3(256), 0,
+                     stream, w.flags, nflags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Steps in groups of UG: before each step of a group, its block column
-  // (and block row of B) receives the group's earlier panels; after the
-  // group, everything further right receives all of the group's panels at
-  // once (K = 64 UG).
-  const int nb = (int)ceil_div(d, NB);
-  for (int g0 = 0; g0 < nb; g0 += UG) {
-    const int gend = std::min(nb, g0 + UG);
-    // the previous group's rest tiles, spread evenly over this group's column
-    // updates (there are UG - 1 of them whenever the rest is not empty)
-    const int rest = g0 > 0 ? rest_tiles(nb, g0) : 0;
-    const int share = (int)ceil_div(rest, UG - 1);
-    for (int k = g0; k < gend; ++k) {
-      // the diagonal block of step k is factorized by the update launch that
-      // brings it up to date (this group's part 1, or the previous group's
-      // part 2); only step 0 needs a launch of its own.  Part 1 also applies
-      // the previous step's panel, so only a group's last step has a panel
-      // launch.
-      if (k > g0) {
-        const int lo = std::min(rest, (k - g0 - 1) * share);
-        const int n = std::min(rest, lo + share) - lo;
-        hipLaunchKernelGGL(fac_colupd_kernel, dim3(nb + n), dim3(256), 0, stream, w.A, w.M,
-                           (const float*)w.Dinv[(k - 1) & 1], w.Dinv[k & 1], d, nb, g0, k, lo,
-                           dev_status);
-      } else if (k == 0) {
-        hipLaunchKernelGGL(fac_diag_kernel, dim3(1), dim3(256), 0, stream, w.A, w.M, w.Dinv[0], d,
-                           k, dev_status);
-      }
-      if (k + 1 < gend) continue;
-      const int nrow = nb - k - 1;
-      if (nrow + k > 0)
-        hipLaunchKernelGGL(fac_panel_kernel, dim3(nrow + k), dim3(256), 0, stream, w.A, w.M,
-                           (const float*)w.Dinv[k & 1], d, k, nrow, (const int32_t*)dev_status);
+  const int64_t spin = spin_limit();
+  for (int c0 = 0; c0 < d; c0 += PW) {
+    const int rows = (int)ceil_div(d - c0, NB);
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(rows), dim3(256), 0, stream, w.A, w.M, w.Dinv,
+                       w.flags, d, c0, dev_status, spin);
+    const int c1 = std::min(d, c0 + PW);
+    if (c1 < d) {
+      const int nt = (int)ceil_div(d - c1, 128);
+      hipLaunchKernelGGL(chol_syrk_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, stream, w.A, d,
+                         c0, c1, (const int32_t*)dev_status);
     }
-    if (gend < nb)
-      hipLaunchKernelGGL(fac_update_kernel, dim3(band_tiles(nb, gend)), dim3(256), 0, stream,
-                         w.A, w.M, w.Dinv[gend & 1], d, nb, g0, gend, dev_status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  for (int s = NB; s < d; s *= 2) {
+    const int sb = s / NB;
+    const int pairs = (int)ceil_div(d - s, 2 * s);  // pairs with b = a + s < d
+    const unsigned tiles = (unsigned)(pairs * sb * sb);
+    hipLaunchKernelGGL(inv_level_kernel<false>, dim3(tiles), dim3(256), 0, stream,
+                       (const float*)w.A, w.M, w.T, d, s, (const int32_t*)dev_status);
+    hipLaunchKernelGGL(inv_level_kernel<true>, dim3(tiles), dim3(256), 0, stream,
+                       (const float*)w.A, w.M, w.T, d, s, (const int32_t*)dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

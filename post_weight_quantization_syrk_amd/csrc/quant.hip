@@ -11,8 +11,9 @@
 //              and each lane applies the feedback to its own 8 columns.  Group
 //              min/max come from a 16-lane butterfly at the group's first column.
 //   trailing : W[:, later columns] -= Err U on the bf16 matrix cores, the
-//              fp32 operands split into bf16 hi + lo and the product formed
-//              in three passes (trailing3_kernel).  Blocks go in groups of four: after
+//              fp32 operands split exactly into three bf16 parts and the
+//              product formed from the six leading part products
+//              (trailing3_kernel), as accurate as an fp32 product.  Blocks go in groups of four: after
 //              each block, its errors update the rest of its group (K = 128);
 //              after the group, all four blocks' errors update every column
 //              after it at once (K = 512), so the bulk of W is read and
@@ -499,19 +500,23 @@ __global__ __launch_bounds__(256) void colloop_kernel(
 }
 
 // Wc[:, n0:n1] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
-// cores: each fp32 operand is split into bf16 hi + lo (hi the nearest bf16,
-// lo the nearest bf16 of the exact remainder) and the product is formed as
-// lo*hi + hi*lo + hi*hi with v_mfma_f32_32x32x16_bf16 into fp32 accumulators,
-// which keeps about 16 significant bits of every product (the dropped lo*lo
-// term and the rounding of lo are below 2^-16 relative); the errors it leaves
-// in the feedback are far below a quantization step.  TM x 64 tiles, K in
-// chunks of 32 (two MFMA steps of 16).  The error tile is stored row-major
+// cores.  Each fp32 operand x is split exactly into three bf16 parts, x = h +
+// m + l (h the nearest bf16 of x, m that of x - h, l that of the remainder,
+// which has at most 8 significant bits left and so is exact), and the product
+// is formed from the six part products that matter,
+//   l*h + h*l + m*m + m*h + h*m + h*h,
+// with v_mfma_f32_32x32x16_bf16 into fp32 accumulators, smallest first.  The
+// dropped terms (m*l, l*m, l*l) come to at most about 2^-23 of the product
+// (|m| <= 2^-8 |x|, |l| <= 2^-16 |x|), so each product carries an error of
+// about one fp32 rounding, as with fp32 FMAs; the
+// feedback is then as exact as fp32 working weights allow.  TM x 64 tiles, K
+// in chunks of 32 (two MFMA steps of 16).  The error tile is stored row-major
 // (k contiguous), the U tile transposed (n-major, k contiguous), so every lane
 // reads its 8 consecutive k as 16 bytes; row pitches of 80 bytes keep those
-// reads free of bank conflicts.  The accumulators start at -Wc and collect
-// Err U, and the tile is stored back negated: negation commutes with every
-// rounding, so this is Wc - Err U as accumulated the other way round, with no
-// negation per staged element.
+// reads free of bank conflicts.  The accumulators start at zero and collect
+// Err U, and Wc - acc is stored: summed onto a preloaded Wc instead, every one
+// of the K roundings would be at the weights' magnitude rather than the
+// products'.
 constexpr int T3K = 32;           // k per chunk
 constexpr int T3P = T3K + 8;      // LDS row pitch (bf16 elements): 80 bytes
 
@@ -522,15 +527,28 @@ __device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
   return __uint_as_float((uint32_t)h << 16);
 }
+// The three-part split of one float (element-wise staging).
+__device__ __forceinline__ uint16_t split3(float x, uint16_t& mid, uint16_t& lo) {
+  const uint16_t hi = bf16_rne_bits(x);
+  const float r = x - bf16_bits_to_f32(hi);
+  mid = bf16_rne_bits(r);
+  lo = bf16_rne_bits(r - bf16_bits_to_f32(mid));
+  return hi;
+}
 // The same split for a pair, with the hardware's nearest-even conversion of
-// two floats at once: hi parts packed low-first, lo parts likewise into lo.
+// two floats at once: each part packed low-first into one word.
 typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& lo) {
+__device__ __forceinline__ f32x2v bf16x2_widen(uint32_t b) {
+  const f32x2v v = {__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)};
+  return v;
+}
+__device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& mid, uint32_t& lo) {
   const f32x2v x = {x0, x1};
   const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
-  const f32x2v hf = {__uint_as_float(hb << 16), __uint_as_float(hb & 0xffff0000u)};
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(x - hf, bf16x2v));
+  const f32x2v r = x - bf16x2_widen(hb);
+  mid = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r - bf16x2_widen(mid), bf16x2v));
   return hb;
 }
 
@@ -547,8 +565,8 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
   constexpr int TN = 64;
   constexpr int NBLK = (TM / 32) * (TN / 32) / 4;  // 32 x 32 blocks per wave
   constexpr int NP = TM * T3K / 256, NQ = T3K * TN / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], al[TM * T3P];
-  __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bl[TN * T3P];
+  __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], amid[TM * T3P], al[TM * T3P];
+  __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bmid[TN * T3P], bl[TN * T3P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int64_t ncols = n1 - n0;
@@ -570,11 +588,7 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
 #pragma unroll
   for (int q = 0; q < NBLK; ++q)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
-      const int c = 32 * bn[q] + l32;
-      acc[q][i] = -C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
-    }
+    for (int i = 0; i < 16; ++i) acc[q][i] = 0.0f;
   const float* P = Err + m0 * d_in + b0;
   const float* Q = U + b0 * d_in + n0t;
   float vp[NP], vq[NQ];
@@ -617,17 +631,19 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
 #pragma unroll
       for (int j = 0; j < NP / 4; ++j) {
         const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
-        uint32_t l0, l1;
-        const uint32_t h0 = split_pair(vp[4 * j], vp[4 * j + 1], l0);
-        const uint32_t h1 = split_pair(vp[4 * j + 2], vp[4 * j + 3], l1);
+        uint32_t m0, m1, l0, l1;
+        const uint32_t h0 = split_pair(vp[4 * j], vp[4 * j + 1], m0, l0);
+        const uint32_t h1 = split_pair(vp[4 * j + 2], vp[4 * j + 3], m1, l1);
         *(uint2*)(ah + r * T3P + c) = make_uint2(h0, h1);
+        *(uint2*)(amid + r * T3P + c) = make_uint2(m0, m1);
         *(uint2*)(al + r * T3P + c) = make_uint2(l0, l1);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint32_t l;
-        const uint32_t hw = split_pair(vq[t], vq[4 + t], l);
+        uint32_t m, l;
+        const uint32_t hw = split_pair(vq[t], vq[4 + t], m, l);
         *(uint32_t*)(bh + (vn + t) * T3P + vk) = hw;
+        *(uint32_t*)(bmid + (vn + t) * T3P + vk) = m;
         *(uint32_t*)(bl + (vn + t) * T3P + vk) = l;
       }
       return;
@@ -636,17 +652,19 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
     for (int u = 0; u < NP; ++u) {
       const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
       const float x = (r < rows && c < kn) ? vp[u] : 0.0f;
-      const uint16_t hi = bf16_rne_bits(x);
-      ah[r * T3P + c] = hi;
-      al[r * T3P + c] = bf16_rne_bits(x - bf16_bits_to_f32(hi));
+      uint16_t mi, lo;
+      ah[r * T3P + c] = split3(x, mi, lo);
+      amid[r * T3P + c] = mi;
+      al[r * T3P + c] = lo;
     }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
       const int e = u * 256 + tid, r = e / TN, c = e % TN;  // r = k, c = n
       const float x = (r < kn && c < cols) ? vq[u] : 0.0f;
-      const uint16_t hi = bf16_rne_bits(x);
-      bh[c * T3P + r] = hi;
-      bl[c * T3P + r] = bf16_rne_bits(x - bf16_bits_to_f32(hi));
+      uint16_t mi, lo;
+      bh[c * T3P + r] = split3(x, mi, lo);
+      bmid[c * T3P + r] = mi;
+      bl[c * T3P + r] = lo;
     }
   };
   gload(0);
@@ -661,21 +679,37 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
 #pragma unroll
       for (int q = 0; q < NBLK; ++q) {
         const int ar = (32 * bm[q] + l32) * T3P + ko, br = (32 * bn[q] + l32) * T3P + ko;
-        const bf16x8 a_h = *(const bf16x8*)(ah + ar), a_l = *(const bf16x8*)(al + ar);
-        const bf16x8 b_h = *(const bf16x8*)(bh + br), b_l = *(const bf16x8*)(bl + br);
+        const bf16x8 a_h = *(const bf16x8*)(ah + ar), a_m = *(const bf16x8*)(amid + ar);
+        const bf16x8 a_l = *(const bf16x8*)(al + ar);
+        const bf16x8 b_h = *(const bf16x8*)(bh + br), b_m = *(const bf16x8*)(bmid + br);
+        const bf16x8 b_l = *(const bf16x8*)(bl + br);
         acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_l, b_h, acc[q], 0, 0, 0);
         acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_l, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_m, b_m, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_m, b_h, acc[q], 0, 0, 0);
+        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_m, acc[q], 0, 0, 0);
         acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_h, acc[q], 0, 0, 0);
       }
     }
   }
+  // the tile's old values, all loads in flight together (clamped addresses),
+  // then Wc - acc
+  float old[NBLK][16];
 #pragma unroll
   for (int q = 0; q < NBLK; ++q)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
       const int c = 32 * bn[q] + l32;
-      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = -acc[q][i];
+      old[q][i] = C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
+    }
+#pragma unroll
+  for (int q = 0; q < NBLK; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
+      const int c = 32 * bn[q] + l32;
+      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = old[q][i] - acc[q][i];
     }
 }
 

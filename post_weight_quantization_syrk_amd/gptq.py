@@ -26,6 +26,20 @@ class GPTQError(RuntimeError):
         self.status = status
 
 
+class SyncTimeoutError(GPTQError):
+    def __init__(self, where: str):
+        RuntimeError.__init__(self, f"{where}: a bounded wait between workgroups expired "
+                                    "(dev_status -1); the factorization did not complete")
+        self.status = GPTQ_EHIP
+
+
+def _raise_status(st: int, where: str):
+    if st > 0:
+        raise NotSPDError(st)
+    if st < 0:
+        raise SyncTimeoutError(where)
+
+
 class NotSPDError(GPTQError):
     def __init__(self, pivot: int):
         RuntimeError.__init__(self, f"gptq_prepare_hinv: Hessian not positive definite "
@@ -155,9 +169,7 @@ def gptq_prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: torch.Tensor | Non
                                    _ptr(ws), nbytes, _stream(stream)), "gptq_prepare_hinv")
     if check:
         (torch.cuda.current_stream() if stream is None else stream).synchronize()
-        st = int(status.item())
-        if st != 0:
-            raise NotSPDError(st)
+        _raise_status(int(status.item()), "gptq_prepare_hinv")
     return U, dead, status
 
 
@@ -281,9 +293,7 @@ def gptq_prepare_hinv_perm(H: torch.Tensor, perm: torch.Tensor | None, damp: flo
            "gptq_prepare_hinv_perm")
     if check:
         (torch.cuda.current_stream() if stream is None else stream).synchronize()
-        st = int(status.item())
-        if st != 0:
-            raise NotSPDError(st)
+        _raise_status(int(status.item()), "gptq_prepare_hinv_perm")
     return U, dead, status
 
 

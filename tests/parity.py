@@ -3,19 +3,28 @@
 Tolerances (GPU vs float64 oracle on the same seeded inputs):
   * Hessian: ||H_gpu - H_ref||_F / ||H_ref||_F <= 1e-4 (lower triangle).
   * Group scales and zeros: identical binary16 values / integers, row by row,
-    up to the row's first divergence.  The GPU carries fp32 working weights;
-    their rounding error (~1e-6 relative after thousands of feedback updates)
-    can move a value across a rounding boundary only when the float64 value
-    sits next to it.  So the first place a row differs -- a scale, a zero or a
-    code -- must be such a near-tie:
-      - scale: the oracle's unrounded step lies within REL_BAND (relative) of
-        the midpoint between the two adjacent binary16 results;
-      - zero: the oracle's unrounded -lo/scale lies within REL_BAND of k + 1/2;
-      - code: the oracle's unrounded quotient w/s lies within Q_BAND of the
-        half-integer between the two codes.
-    After that point the row legitimately follows a different greedy path
-    (the error fed forward differs by one grid step), so later scale/zero
-    differences in that row are counted, not failed.
+    up to the row's first divergence.  The GPU carries fp32 working weights,
+    so a working value x differs from the oracle's by a rounding error; call
+    its size, in grid steps of the value's group, eta.  A rounding decision
+    can then come out differently only when the float64 quantity sits within
+    that error of the decision boundary, and the three boundaries follow from
+    the one budget:
+      - code: the quotient x/s lies within ETA of the half-integer between
+        the two codes (x moves by eta steps, x/s by eta);
+      - zero: -lo/s lies within 3 ETA of k + 1/2 (lo moves by eta steps, and s
+        by the relative amount below, which moves -lo/s by at most 2 eta more
+        since |lo/s| <= maxq);
+      - scale: the unrounded step (hi - lo)/maxq, or 2 max|v|/maxq, lies
+        within 2 ETA / maxq (relative) of the midpoint between the two
+        adjacent binary16 values (hi and lo each move by eta steps).
+    ETA = 2e-4 steps is 13x the largest working-value error that fp32
+    arithmetic of this kind (fp32 column loop, trailing update with products
+    as exact as fp32) makes before a row's first divergence: 1.6e-5 steps,
+    measured by emulating that arithmetic on the CPU for 8192-column rows of
+    the 70B-shaped layer (4-bit g128; 3.5e-6 at 2-bit g32).
+    After that point the row legitimately follows another greedy path (the
+    error fed forward differs by one grid step), so later scale/zero
+    differences in that row are counted, not failed, and bounded in number.
   * Codes: at most 0.5% of all codes differ.  Where a group's scale and zero
     agree, a differing code differs by exactly 1.  In a group whose parameters
     moved (only possible downstream of an admissible first divergence) codes
@@ -29,8 +38,7 @@ from __future__ import annotations
 
 import numpy as np
 
-REL_BAND = 2e-5
-Q_BAND = 2e-4
+ETA = 2e-4   # working-value error budget, in grid steps
 
 
 def h_rel_error(H_gpu: np.ndarray, H_ref: np.ndarray) -> float:
@@ -48,21 +56,21 @@ def dequant(codes, scales, zeros, group_size):
     return s * (codes - z)
 
 
-def _scale_near_tie(sg, sr, raw):
+def _scale_near_tie(sg, sr, raw, maxq):
     lo, hi = sorted((float(sg), float(sr)))
     nxt = float(np.nextafter(np.float16(lo), np.float16(np.inf)))
-    return hi == nxt and abs(raw - 0.5 * (lo + nxt)) <= REL_BAND * raw
+    return hi == nxt and abs(raw - 0.5 * (lo + nxt)) <= 2.0 * ETA / maxq * raw
 
 
 def _zero_near_tie(zg, zr, raw):
     k = min(zg, zr)
-    return abs(zg - zr) == 1 and abs(raw - (k + 0.5)) <= REL_BAND * max(1.0, abs(raw))
+    return abs(zg - zr) == 1 and abs(raw - (k + 0.5)) <= 3.0 * ETA
 
 
 def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H0=None,
                   max_code_frac: float = 0.005, loss_rtol: float = 1e-3,
                   max_row_frac: float = 0.05, max_param_frac: float = 0.01,
-                  max_moved_steps: float = 2.5) -> dict:
+                  max_moved_steps: float = 2.0) -> dict:
     """Check GPU quantizer outputs against the oracle's; returns a report dict.
 
     gpu: codes, scales, zeros (numpy).  ref: the oracle's gptq() result.
@@ -102,7 +110,7 @@ def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H
         if first_p <= first_c:  # parameters differ first (at a group start)
             g = first_p // G
             if sg[r, g] != sr[r, g]:
-                ok = _scale_near_tie(sg[r, g], sr[r, g], ref["raw_scales"][r, g])
+                ok = _scale_near_tie(sg[r, g], sr[r, g], ref["raw_scales"][r, g], maxq)
             else:
                 ok = _zero_near_tie(zg[r, g], zr[r, g], ref["raw_zeros"][r, g])
             what = ("param", g, float(sg[r, g]), float(sr[r, g]), float(zg[r, g]), float(zr[r, g]))
@@ -112,7 +120,7 @@ def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H
             k = min(cg[r, j], cr[r, j])
             boundary = (k - zr[r, g]) + 0.5
             rq = ref["raw_q"][r, j]
-            ok = abs(cg[r, j] - cr[r, j]) == 1 and abs(rq - boundary) <= Q_BAND
+            ok = abs(cg[r, j] - cr[r, j]) == 1 and abs(rq - boundary) <= ETA
             what = ("code", j, int(cg[r, j]), int(cr[r, j]), float(rq))
         if not ok:
             bad.append((int(r),) + what)
@@ -131,19 +139,41 @@ def compare_quant(gpu: dict, ref: dict, *, group_size: int, bits: int, W=None, H
         problems.append("code out of range")
     if rep["code_max_diff"] > 1:
         problems.append("code differs by more than 1 under identical group parameters")
-    # a moved group lies after the row's first (admissible) divergence: the two
-    # sides' values come from different greedy paths, each within half a step
-    # of its own compensated weight; 2.5 steps is a sanity bound, not an
-    # arithmetic one
+    # a moved group lies after the row's first (admissible) divergence: see
+    # the module docstring for the two-step bound
     if rep["moved_group_max_steps"] > max_moved_steps:
         problems.append("dequantized value off by more than max_moved_steps in a moved group")
     if rep["param_mismatch"] > max_param_frac * rep["groups"]:
         problems.append("too many groups with moved parameters")
     if rep["code_diff_frac"] > max_code_frac:
         problems.append("too many differing codes")
-    if d_out and rows.size > max(1, max_row_frac * d_out):
+    # each row takes d_in rounding decisions, each with a small chance of
+    # sitting within the working-value error of a boundary, so the expected
+    # share of rows that diverge grows with the row length: the bar is
+    # max_row_frac at 4096 columns and scales linearly above that
+    row_bar = max_row_frac * max(1.0, d_in / 4096.0)
+    rep["row_bar"] = row_bar
+    if d_out and rows.size > max(1, row_bar * d_out):
         problems.append("too many diverged rows")
     if "loss_rel" in rep and rep["loss_rel"] > loss_rtol:
         problems.append("layer loss outside tolerance")
     assert not problems, (problems, rep)
     return rep
+
+
+def check_row_losses(gpu_loss, gpu: dict, ref: dict, rtol: float = 1e-4,
+                     layer_rtol: float = 1e-3):
+    """The damped loss sum_j delta_j^2 per row (the quantizer's loss_rows) against
+    the oracle's.  A row whose codes and parameters all agree took the same
+    greedy path, so its loss differs only by fp32 rounding of d_in squared
+    terms (relative error far below rtol); a row that diverged (admissibly, at
+    a near-tie) then follows another path and only enters the layer total,
+    which stays within layer_rtol."""
+    gl = np.asarray(gpu_loss, np.float64)
+    rl = np.asarray(ref["loss_damped"], np.float64)
+    same = ~((np.asarray(gpu["codes"]) != np.asarray(ref["codes"])).any(axis=1)
+             | (np.asarray(gpu["scales"]) != np.asarray(ref["scales"])).any(axis=1)
+             | (np.asarray(gpu["zeros"]) != np.asarray(ref["zeros"])).any(axis=1))
+    np.testing.assert_allclose(gl[same], rl[same], rtol=rtol)
+    assert abs(gl.sum() - rl.sum()) <= layer_rtol * abs(rl.sum())
+    return int(same.sum())

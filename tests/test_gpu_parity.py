@@ -8,7 +8,7 @@ import torch
 
 import oracle
 from post_weight_quantization_syrk_amd import gptq, synth
-from parity import compare_quant, h_rel_error
+from parity import check_row_losses, compare_quant, h_rel_error
 
 pytestmark = pytest.mark.gpu
 
@@ -274,8 +274,9 @@ def test_quantize_parity_correlated(bits, g, sym):
     rep = compare_quant(out, ref, group_size=g, bits=bits, W=W.astype(np.float64),
                         H0=H32.astype(np.float64))
     print(f"[quant] bits={bits} g={g} sym={sym} {rep}", flush=True)
-    # the damped-H loss identity holds on the GPU side too
-    np.testing.assert_allclose(out["loss"], ref["loss_damped"], rtol=5e-3)
+    # the damped-H loss identity holds on the GPU side too (rows on the same
+    # greedy path to fp32 rounding; the layer total within 1e-3)
+    check_row_losses(out["loss"], out, ref)
 
 
 @pytest.mark.parametrize("d_in,wdt", [(256, "f32"), (256, "bf16"), (100, "f32"), (100, "bf16")])
@@ -456,16 +457,7 @@ def test_70b_shape_layer_sampled_rows():
         ref = oracle.gptq(W64[rows], p["U"], p["dead"], bits=bits, group_size=g, sym=False,
                           block=128)
         sub_out = {k: v[rows] for k, v in out.items()}
-        # 8192-column rows and kappa ~7.5e4 (U error ~3x the attention case):
-        # most rows meet a near-tie that the two computations decide
-        # differently (at 2 bits about half of them), after which a row
-        # follows another greedy path.  Every row's first divergence is still
-        # checked to be a near-tie, codes differ by at most 1 under equal
-        # parameters, moved groups stay within two steps and the layer loss
-        # within 1e-3; only the counts of diverged rows, codes and moved
-        # parameters are wider than for 4096-column rows.
-        rep = compare_quant(sub_out, ref, group_size=g, bits=bits, W=W64[rows], H0=H0r,
-                            max_row_frac=1.0, max_code_frac=0.02, max_param_frac=0.1)
+        rep = compare_quant(sub_out, ref, group_size=g, bits=bits, W=W64[rows], H0=H0r)
         print(f"[70b] bits={bits} g={g} {rep}", flush=True)
 
 
