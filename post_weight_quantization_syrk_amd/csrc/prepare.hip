@@ -16,7 +16,9 @@
 //     workgroups handing results to each other through release/acquire flags
 //     with bounded waits.  Each workgroup keeps its row block's panel columns
 //     in registers for the whole panel.  After the panel, the trailing matrix
-//     receives the panel at once (chol_syrk_kernel, K = 256).
+//     receives the panel at once (K = 256): the next panel's columns right
+//     away (chol_band_kernel), the rest by extra workgroups of the next
+//     panel's launch.
 //   Inverse, by recursive doubling: with the diagonal blocks' inverses from the
 //     panels, blocks of size s pair up into blocks of 2s,
 //       inv([L11 0; L21 L22]) = [X11 0; -X22 L21 X11  X22],
@@ -425,23 +427,41 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
 
 
 // ---- synchronisation between the workgroups of one panel launch ----------
-// Flags live in the workspace and are cleared before the panels start.  A
-// producer writes its results, makes them visible device-wide (release fence
-// by every thread, then a release store of the flag); a consumer's thread 0
-// polls the flag with acquire loads, every thread then takes an acquire fence
-// before reading the results.  Every wait is bounded: it also stops when the
-// factorization has failed (dev_status set by another workgroup) or after
-// `spin` polls, which sets dev_status to SYNC_TIMEOUT; either way the
-// workgroup leaves, so the launch always drains.
+// Everything one workgroup hands to another inside a launch -- the diagonal
+// block's inverse, the panel's blocks of L, the flags, a failure status -- is
+// written and read with system-coherent accesses, which bypass the per-XCD L2
+// caches.  With ordinary accesses and device-scope release/acquire fences, a
+// reader on another XCD was measured to see stale data (wrong factors that
+// varied from call to call); with coherent accesses the results are
+// bit-reproducible.  A producer waits for its own stores to complete, the
+// workgroup meets at a barrier, then one thread sets the flag (no cache-wide
+// writeback).  A consumer's thread 0 polls the flag, then every thread takes
+// an acquire fence, which drops stale copies from its XCD's L2 (measured:
+// without it a reader could still see data from before the producer's
+// write).  Every wait is bounded: it also stops when the factorization has
+// failed (dev_status set by another workgroup) or after `spin` polls, which
+// sets dev_status to SYNC_TIMEOUT; either way the workgroup leaves, so the
+// launch always drains.  Flags live in the workspace and are cleared before
+// the panels start.
 __global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int64_t n) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
     p[e] = 0;
 }
 
+__device__ __forceinline__ void xstore2(float* p, float a, float b) {
+  const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
+  __hip_atomic_store((uint64_t*)p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ float2 xload2(const float* p) {
+  const uint64_t v =
+      __hip_atomic_load((const uint64_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+  return make_float2(__uint_as_float((uint32_t)v), __uint_as_float((uint32_t)(v >> 32)));
+}
+
 __device__ __forceinline__ void publish(int* flag) {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this thread's stores are done
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  if (threadIdx.x == 0) __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 __device__ __forceinline__ bool wait_flag(const int* flag, int32_t* status, int64_t spin,
@@ -449,8 +469,8 @@ __device__ __forceinline__ bool wait_flag(const int* flag, int32_t* status, int6
   if (threadIdx.x == 0) {
     int ok = 1;
     for (int64_t it = 0;; ++it) {
-      if (__hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM) != 0) break;
-      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+      if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) break;
+      if (__hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) {
         ok = 0;
         break;
       }
@@ -459,12 +479,15 @@ __device__ __forceinline__ bool wait_flag(const int* flag, int32_t* status, int6
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
-    if (ok && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) ok = 0;
+    if (ok && __hip_atomic_load(status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) != 0) ok = 0;
     *ok_lds = ok;
   }
   __syncthreads();
+  // Coherent stores bypass the L2 without invalidating a copy that an earlier
+  // ordinary load left in this XCD's L2; an acquire at device scope drops
+  // such copies before the reads.
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
   const bool ok = *ok_lds != 0;
   __syncthreads();  // everyone has read ok_lds before it is written again
@@ -514,31 +537,45 @@ __device__ __forceinline__ void stage_q_regs(float* lds, const f32x16& a, int ro
   });
 }
 
-// Blocks handed from one workgroup to another inside a launch are written and
-// read with system-coherent accesses, which bypass the per-XCD L2 caches:
-// with ordinary accesses, release/acquire at device scope was measured to let
-// a reader on another XCD see stale data (wrong factors, varying from call to
-// call), and with these accesses the results are bit-reproducible.
-__device__ __forceinline__ void xstore(float* p, float v) {
-  __hip_atomic_store((uint32_t*)p, __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+__device__ __forceinline__ void xstore1(float* p, float a) {
+  __hip_atomic_store((uint32_t*)p, __float_as_uint(a), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
-__device__ __forceinline__ float xload(const float* p) {
+__device__ __forceinline__ float xload1(const float* p) {
   return __uint_as_float(
       __hip_atomic_load((const uint32_t*)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM));
 }
-// Q^T operand (rows x cols valid, zero outside) from another workgroup's block.
+
+// Q^T operand (rows x cols valid, zero outside) from another workgroup's
+// block, read coherently: in 8-byte pairs when the rows are 8-byte aligned
+// (even leading dimension and base), else one element at a time.
 __device__ __forceinline__ void load_q_xchg(float* lds, const float* src, int64_t ld, int rows,
                                             int cols) {
+  float* q0 = lds + TileT::lds_q_offset;
+  if ((ld & 1) == 0 && ((uintptr_t)src & 7) == 0) {
+    float2 v[NB * NB / 512];
+#pragma unroll
+    for (int u = 0; u < NB * NB / 512; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / (NB / 2), c = 2 * (e % (NB / 2));
+      v[u] = xload2(src + (int64_t)min(r, rows - 1) * ld + min(c, (cols - 1) & ~1));
+    }
+#pragma unroll
+    for (int u = 0; u < NB * NB / 512; ++u) {
+      const int e = u * 256 + threadIdx.x, r = e / (NB / 2), c = 2 * (e % (NB / 2));
+      q0[r * TileT::QPITCH + c] = (r < rows && c < cols) ? v[u].x : 0.0f;
+      q0[r * TileT::QPITCH + c + 1] = (r < rows && c + 1 < cols) ? v[u].y : 0.0f;
+    }
+    return;
+  }
   float v[NB * NB / 256];
 #pragma unroll
   for (int u = 0; u < NB * NB / 256; ++u) {
     const int e = u * 256 + threadIdx.x, r = e / NB, c = e % NB;
-    v[u] = xload(src + (int64_t)min(r, rows - 1) * ld + min(c, cols - 1));
+    v[u] = xload1(src + (int64_t)min(r, rows - 1) * ld + min(c, cols - 1));
   }
 #pragma unroll
   for (int u = 0; u < NB * NB / 256; ++u) {
     const int e = u * 256 + threadIdx.x, r = e / NB, c = e % NB;
-    lds[TileT::lds_q_offset + r * TileT::QPITCH + c] = (r < rows && c < cols) ? v[u] : 0.0f;
+    q0[r * TileT::QPITCH + c] = (r < rows && c < cols) ? v[u] : 0.0f;
   }
 }
 
@@ -546,16 +583,33 @@ __device__ __forceinline__ void mma1(const float* lds, f32x16& acc) {
   TileT::mma(lds, *reinterpret_cast<f32x16(*)[1][1]>(&acc));
 }
 
+template <int TS>
+__device__ __forceinline__ void syrk_tile(float* __restrict__ A, int d, int c0, int c1, int i0,
+                                          int j0, float* lds);
+
+constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
+
+// Workgroups past the panel's row blocks (blockIdx.x >= rows) are passengers:
+// they apply the previous panel [pc0, c0) to the trailing tiles from c0 + PW on
+// (128 x 128 lower tiles of that region), which this panel does not touch.
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
                                                          float* __restrict__ M,
                                                          float* __restrict__ Dinv,
                                                          int* __restrict__ flags, int d, int c0,
+                                                         int rows, int pc0,
                                                          int32_t* status, int64_t spin) {
   if (*status != 0) return;
-  constexpr size_t LDS_FLOATS = TileT::lds_floats > DIAG_LDS_FLOATS ? TileT::lds_floats
-                                                                      : DIAG_LDS_FLOATS;
+  constexpr size_t LDS_FLOATS =
+      cmax(cmax(TileT::lds_floats, DIAG_LDS_FLOATS), MfmaTile<128, 128, 32, true>::lds_floats);
   __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
   __shared__ int ok_lds;
+  if ((int)blockIdx.x >= rows) {
+    int ti, tj;
+    tri_coords((int)blockIdx.x - rows, ti, tj);
+    const int r0 = c0 + PW;
+    syrk_tile<128>(A, d, pc0, c0, r0 + 128 * ti, r0 + 128 * tj, lds);
+    return;
+  }
   const int r = blockIdx.x;
   const int pw = min(PW, d - c0), nj = (pw + NB - 1) / NB;
   const int i0 = c0 + NB * r, ib = min(NB, d - i0);
@@ -588,9 +642,14 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
       for (int e = threadIdx.x; e < NB * (NB + 1); e += 256) (&L.mtile[0][0])[e] = 0.0f;
       __syncthreads();
       diag_factor(L, A, M, Dinv + (size_t)kg * NB * NB, d, kg, status);
-      // the inverse again, for the other workgroups, from its LDS copy
-      for (int e = threadIdx.x; e < NB * NB; e += 256)
-        xstore(Dinv + (size_t)kg * NB * NB + e, L.mtile[e / NB][e % NB]);
+      // the inverse again, for the other workgroups, from its LDS copy, and
+      // a failure made visible to them
+      for (int e = threadIdx.x; e < NB * NB / 2; e += 256) {
+        const int rr = e / (NB / 2), cc = 2 * (e % (NB / 2));
+        xstore2(Dinv + (size_t)kg * NB * NB + rr * NB + cc, L.mtile[rr][cc], L.mtile[rr][cc + 1]);
+      }
+      if (threadIdx.x == 0 && *status != 0)
+        __hip_atomic_store(status, *status, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       publish(fdiag + j);
       done = true;
       return;
@@ -607,14 +666,31 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
     mma1(lds, acc[j]);
     __syncthreads();
     float* Arj = A + (int64_t)i0 * d + k0;
-    acc_each(acc[j], [&](int row, int col, int q) {
-      if (row < ib && col < kb) {
-        if (r < nj)
-          xstore(Arj + (int64_t)row * d + col, acc[j][q]);
-        else
-          Arj[(int64_t)row * d + col] = acc[j][q];
+    if (r < nj) {
+      // through LDS (the P slot, free after the product) into coherent pairs
+      acc_each(acc[j], [&](int row, int col, int q) { lds[row * TileT::PP + col] = acc[j][q]; });
+      __syncthreads();
+      if ((d & 1) == 0) {  // rows 8-byte aligned: coherent pairs
+        for (int e = threadIdx.x; e < NB * NB / 2; e += 256) {
+          const int rr = e / (NB / 2), cc = 2 * (e % (NB / 2));
+          if (rr < ib && cc + 1 < kb)
+            xstore2(Arj + (int64_t)rr * d + cc, lds[rr * TileT::PP + cc],
+                    lds[rr * TileT::PP + cc + 1]);
+          else if (rr < ib && cc < kb)
+            xstore1(Arj + (int64_t)rr * d + cc, lds[rr * TileT::PP + cc]);
+        }
+      } else {
+        for (int e = threadIdx.x; e < NB * NB; e += 256) {
+          const int rr = e / NB, cc = e % NB;
+          if (rr < ib && cc < kb) xstore1(Arj + (int64_t)rr * d + cc, lds[rr * TileT::PP + cc]);
+        }
       }
-    });
+      __syncthreads();
+    } else {
+      acc_each(acc[j], [&](int row, int col, int q) {
+        if (row < ib && col < kb) Arj[(int64_t)row * d + col] = acc[j][q];
+      });
+    }
     if (r < nj) publish(fcol + j * NJ + r);
     // later panel columns of this row block: A_{r,jj} -= L_rj L_{jj,j}^T
     StaticFor<j + 1, NJ>::run([&](auto JJ) {
@@ -642,29 +718,29 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
   });
 }
 
-// Trailing update after a panel: A[c1:, c1:] (lower tiles) -= P P^T with
-// P = L[c1:, c0:c1] (K = c1 - c0 <= 256), 128 x 128 tiles, K in chunks of 32;
-// the next chunk's operands are loaded while the current one multiplies.  The
+// Trailing update after a panel [c0, c1): A[c1:, c1:] (lower) -= P P^T with
+// P = L[c1:, c0:c1] (K = c1 - c0 <= 256), in TS x TS tiles, K in chunks of 32,
+// the next chunk's operands loaded while the current one multiplies.  The
 // products are summed from zero and subtracted from A once: summed onto a
 // preloaded A, every one of the K roundings would be at A's magnitude, which
 // on the large diagonal entries grows the factor's error like sqrt(d) u |A|.
 // Diagonal tiles are computed whole (their upper halves land in A's unused
-// upper triangle).
-using TileS = MfmaTile<128, 128, 32, true>;
-
-__global__ __launch_bounds__(256) void chol_syrk_kernel(float* __restrict__ A, int d, int c0,
-                                                        int c1, const int32_t* status) {
-  if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[TileS::lds_floats];
-  int ti, tj;
-  tri_coords(blockIdx.x, ti, tj);
-  const int i0 = c1 + 128 * ti, j0 = c1 + 128 * tj;
-  const int ib = min(128, d - i0), jb = min(128, d - j0);
+// upper triangle).  The update is split in two: the band -- the next panel's
+// columns [c1, c1 + PW), all rows below -- runs right after the panel
+// (chol_band_kernel, 64 x 64 tiles); the rest -- rows and columns from
+// c1 + PW on, which nothing reads before the panel after next -- runs as
+// extra workgroups of the next panel's launch (128 x 128 tiles), on the
+// compute units its latency-bound chain leaves idle.
+template <int TS>
+__device__ __forceinline__ void syrk_tile(float* __restrict__ A, int d, int c0, int c1, int i0,
+                                          int j0, float* lds) {
+  using TileS = MfmaTile<TS, TS, 32, true>;
+  const int ib = min(TS, d - i0), jb = min(TS, d - j0);
   const int kw = c1 - c0;
   float* C = A + (int64_t)i0 * d + j0;
   f32x16 acc[TileS::FM][TileS::FN];
   TileS::zero(acc);
-  TileS::PQRegs v;
+  typename TileS::PQRegs v;
   auto fetch = [&](int kc) __attribute__((always_inline)) {
     const int kn = min(32, kw - kc);
     TileS::fetch_pq(v, A + (int64_t)i0 * d + c0 + kc, d, ib, kn,
@@ -674,60 +750,71 @@ __global__ __launch_bounds__(256) void chol_syrk_kernel(float* __restrict__ A, i
   for (int kc = 0; kc < kw; kc += 32) {
     const int kn = min(32, kw - kc);
     if (kc > 0) __syncthreads();
-    TileS::stage_pq<false>(lds, v, ib, kn, jb, kn);
+    TileS::template stage_pq<false>(lds, v, ib, kn, jb, kn);
     __syncthreads();
     if (kc + 32 < kw) fetch(kc + 32);
     TileS::mma(lds, acc);
   }
-  TileS::store<true>(C, d, ib, jb, acc);
+  TileS::template store<true>(C, d, ib, jb, acc);
+}
+
+// The band after panel [c0, c1): tiles (rows c1 + 64 i, columns c1 + 64 j) of
+// the next panel's columns, lower ones only.
+__global__ __launch_bounds__(256) void chol_band_kernel(float* __restrict__ A, int d, int c0,
+                                                        int c1, int nbc, const int32_t* status) {
+  if (*status != 0) return;
+  __shared__ __attribute__((aligned(16))) float lds[MfmaTile<64, 64, 32, true>::lds_floats];
+  const int i = blockIdx.x / nbc, j = blockIdx.x % nbc;
+  if (j > i) return;
+  syrk_tile<64>(A, d, c0, c1, c1 + 64 * i, c1 + 64 * j, lds);
 }
 
 // ---- the inverse: recursive doubling ------------------------------------
 // Level s (a power of two times 64): pairs (a, b = a + s, e = min(b + s, d)),
-// a = 0, 2s, 4s, ..., b < d.  Tile (rt, ct) of a pair covers rows
-// b + 64 rt .. and columns a + 64 ct ..; (s / 64)^2 tiles per pair.
-//   inv_t_kernel: T[b:e, a:b] = L[b:e, a:b] M[a:b, a:b]   (M lower: m >= ct)
-//   inv_x_kernel: M[b:e, a:b] = -M[b:e, b:e] T[b:e, a:b]  (M lower: m <= rt)
-using TileN = MfmaTile<NB, NB, NB, false>;  // C = P Q with Q row-major
-
+// a = 0, 2s, 4s, ..., b < d.  Tile (rt, ct) of a pair covers rows b + 64 rt ..
+// and columns a + 64 ct ..; (s / 64)^2 tiles per pair.
+//   T step: T[b:e, a:b] = L[b:e, a:b] M[a:b, a:b]   (M lower: k >= 64 ct)
+//   X step: M[b:e, a:b] = -M[b:e, b:e] T[b:e, a:b]  (M lower: k < 64 rt + 64)
+// A tile's work grows with its K range (the triangle), so workgroups are
+// numbered longest tile first (ct ascending for T, rt descending for X).
 template <bool XSTEP>
 __global__ __launch_bounds__(256) void inv_level_kernel(const float* __restrict__ L,
                                                         float* __restrict__ M,
-                                                        float* __restrict__ T, int d, int s,
-                                                        const int32_t* status) {
+                                                        float* __restrict__ Tb, int d, int s,
+                                                        int pairs, const int32_t* status) {
+  using Tile = MfmaTile<NB, NB, 32, false>;  // C = P Q with Q row-major
   if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[TileN::lds_floats];
-  const int sb = s / NB;  // blocks per half
+  __shared__ __attribute__((aligned(16))) float lds[Tile::lds_floats];
+  const int sb = s / NB;  // tiles per half
   const int t = blockIdx.x;
-  const int p = t / (sb * sb), rem = t % (sb * sb), rt = rem / sb, ct = rem % sb;
+  const int major = t / (pairs * sb), rem = t % (pairs * sb);
+  const int p = rem / sb, minor = rem % sb;
+  const int rt = XSTEP ? sb - 1 - major : minor, ct = XSTEP ? minor : major;
   const int a = 2 * s * p, b = a + s;
   const int i0 = b + NB * rt, j0 = a + NB * ct;
   if (i0 >= d) return;
   const int ib = min(NB, d - i0);
-  // K range, in blocks: T step m = ct .. sb-1 over L[i0, a + 64 m] M[a + 64 m, j0];
-  // X step m = 0 .. rt over M[i0, b + 64 m] T[b + 64 m, j0]
-  const int m_lo = XSTEP ? 0 : ct, m_hi = XSTEP ? rt : sb - 1;
+  const int k_lo = XSTEP ? 0 : NB * ct, k_hi = XSTEP ? min(NB * rt + NB, d - b) : s;
   const float* Pb = XSTEP ? M + (int64_t)i0 * d + b : L + (int64_t)i0 * d + a;
-  const float* Qb = XSTEP ? T + (int64_t)b * d + j0 : M + (int64_t)a * d + j0;
-  const int qbase = XSTEP ? b : a;
-  f32x16 acc[TileN::FM][TileN::FN];
-  TileN::zero(acc);
-  TileN::PQRegs v;
-  auto fetch = [&](int m) __attribute__((always_inline)) {
-    const int mb = min(NB, d - (qbase + NB * m));
-    TileN::fetch_pq(v, Pb + NB * m, d, ib, mb, Qb + (int64_t)NB * m * d, d, mb, NB);
+  const float* Qb = XSTEP ? Tb + (int64_t)b * d + j0 : M + (int64_t)a * d + j0;
+  f32x16 acc[Tile::FM][Tile::FN];
+  Tile::zero(acc);
+  typename Tile::PQRegs v;
+  auto fetch = [&](int k) __attribute__((always_inline)) {
+    const int kn = min(32, k_hi - k);
+    Tile::fetch_pq(v, Pb + k, d, ib, kn, Qb + (int64_t)k * d, d, kn, NB);
   };
-  fetch(m_lo);
-  for (int m = m_lo; m <= m_hi; ++m) {
-    const int mb = min(NB, d - (qbase + NB * m));
-    if (m > m_lo) __syncthreads();
-    TileN::stage_pq<XSTEP>(lds, v, ib, mb, mb, NB);
+  fetch(k_lo);
+  for (int k = k_lo; k < k_hi; k += 32) {
+    const int kn = min(32, k_hi - k);
+    if (k > k_lo) __syncthreads();
+    Tile::template stage_pq<XSTEP>(lds, v, ib, kn, kn, NB);
     __syncthreads();
-    if (m + 1 <= m_hi) fetch(m + 1);
-    TileN::mma(lds, acc);
+    if (k + 32 < k_hi) fetch(k + 32);
+    Tile::mma(lds, acc);
   }
-  float* C = (XSTEP ? M : T) + (int64_t)i0 * d + j0;
-  TileN::store<false>(C, d, ib, NB, acc);
+  float* C = (XSTEP ? M : Tb) + (int64_t)i0 * d + j0;
+  Tile::template store<false>(C, d, ib, NB, acc);
 }
 
 // U[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -786,25 +873,32 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
   const int64_t spin = spin_limit();
   for (int c0 = 0; c0 < d; c0 += PW) {
     const int rows = (int)ceil_div(d - c0, NB);
-    hipLaunchKernelGGL(chol_panel_kernel, dim3(rows), dim3(256), 0, stream, w.A, w.M, w.Dinv,
-                       w.flags, d, c0, dev_status, spin);
+    // passengers: the previous panel's update of the region from c0 + PW on
+    int rest = 0;
+    if (c0 > 0 && c0 + PW < d) {
+      const int nt = (int)ceil_div(d - c0 - PW, 128);
+      rest = nt * (nt + 1) / 2;
+    }
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(rows + rest), dim3(256), 0, stream, w.A, w.M,
+                       w.Dinv, w.flags, d, c0, rows, c0 - PW, dev_status, spin);
     const int c1 = std::min(d, c0 + PW);
-    if (c1 < d) {
-      const int nt = (int)ceil_div(d - c1, 128);
-      hipLaunchKernelGGL(chol_syrk_kernel, dim3(nt * (nt + 1) / 2), dim3(256), 0, stream, w.A, d,
-                         c0, c1, (const int32_t*)dev_status);
+    if (c1 < d) {  // the band: the next panel's columns
+      const int nr = (int)ceil_div(d - c1, 64);
+      const int nbc = (int)ceil_div(std::min(d, c1 + PW) - c1, 64);
+      hipLaunchKernelGGL(chol_band_kernel, dim3(nr * nbc), dim3(256), 0, stream, w.A, d, c0, c1,
+                         nbc, (const int32_t*)dev_status);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   for (int s = NB; s < d; s *= 2) {
-    const int sb = s / NB;
     const int pairs = (int)ceil_div(d - s, 2 * s);  // pairs with b = a + s < d
+    const int sb = s / NB;
     const unsigned tiles = (unsigned)(pairs * sb * sb);
     hipLaunchKernelGGL(inv_level_kernel<false>, dim3(tiles), dim3(256), 0, stream,
-                       (const float*)w.A, w.M, w.T, d, s, (const int32_t*)dev_status);
+                       (const float*)w.A, w.M, w.T, d, s, pairs, (const int32_t*)dev_status);
     hipLaunchKernelGGL(inv_level_kernel<true>, dim3(tiles), dim3(256), 0, stream,
-                       (const float*)w.A, w.M, w.T, d, s, (const int32_t*)dev_status);
+                       (const float*)w.A, w.M, w.T, d, s, pairs, (const int32_t*)dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
