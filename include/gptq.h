@@ -73,6 +73,31 @@ int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype,
 size_t gptq_hessian_workspace(int64_t d, int64_t n_tokens, int x_dtype);
 
 /* ---------------------------------------------------------------------------
+ * gptq_hessian_accumulate without a workspace argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * or calibration loops, harnesses that forbid allocation): the same
+ * H += 2 X^T X with the same arguments, but the split-K partial tiles live in
+ * a fixed array of gptq_noalloc_scratch_bytes() (64 MiB) that the library
+ * holds on each GPU it runs on, from its load until the process ends.  This
+ * call allocates and frees nothing.
+ *
+ * The number of token splits is capped so that the partials fit the array:
+ * with bf16 X (256 x 256 tiles) d <= 5632, with fp32 X (64 x 64 tiles)
+ * d <= 5760; larger d returns GPTQ_EUNSUPPORTED before anything is enqueued.
+ * When the cap does not bind (small d or few tokens) the split count, and so
+ * the result, is bit-identical to gptq_hessian_accumulate's; otherwise the
+ * same sums are formed in another split order.
+ * Every call on one GPU uses that GPU's one array: calls that overlap in time
+ * on the same GPU (different streams, or different host threads without
+ * ordering) race on it and give wrong results.  Calls on one stream are
+ * ordered and safe; every partial tile is rewritten by each call, so nothing
+ * carries over from the previous call.
+ * ------------------------------------------------------------------------- */
+int gptq_hessian_accumulate_noalloc(float* H, int64_t d, const void* X, int x_dtype,
+                                    int64_t n_tokens, int64_t ldx, gptq_stream stream);
+size_t gptq_noalloc_scratch_bytes(void);
+
+/* ---------------------------------------------------------------------------
  * Damping, Cholesky and the upper factor of the inverse.  [P1] 阶段一 (H ~
  * 2X^T X + lambda I, then a Cholesky factorization whose triangular factor is
  * used row by row instead of a full inverse).

@@ -56,6 +56,25 @@ int gptq_hessian_accumulate(float* H, int64_t d, const void* X, int x_dtype, int
       gptq::syrk_launch(H, d, X, x_dtype, n_tokens, ldx, ws, plan, (hipStream_t)stream));
 }
 
+int gptq_hessian_accumulate_noalloc(float* H, int64_t d, const void* X, int x_dtype,
+                                    int64_t n_tokens, int64_t ldx, gptq_stream stream) {
+  if (d <= 0 || d > (int64_t)1 << 20 || n_tokens < 0 || ldx < d) return GPTQ_EINVAL;
+  if (x_dtype != GPTQ_BF16 && x_dtype != GPTQ_F32) return GPTQ_EINVAL;
+  if (!H) return GPTQ_EINVAL;
+  if (n_tokens == 0) return GPTQ_OK;
+  if (!X) return GPTQ_EINVAL;
+  const gptq::SyrkPlan plan =
+      gptq::syrk_plan_capped(d, n_tokens, x_dtype, gptq::NOALLOC_SCRATCH_BYTES);
+  if (plan.splits < 1) return GPTQ_EUNSUPPORTED;  // one split's partials exceed the array
+  void* scratch = nullptr;
+  const hipError_t e = gptq::syrk_scratch(&scratch);
+  if (e != hipSuccess) return GPTQ_EHIP;
+  return hip_status(
+      gptq::syrk_launch(H, d, X, x_dtype, n_tokens, ldx, scratch, plan, (hipStream_t)stream));
+}
+
+size_t gptq_noalloc_scratch_bytes(void) { return gptq::NOALLOC_SCRATCH_BYTES; }
+
 size_t gptq_prepare_workspace(int64_t d) {
   if (d <= 0) return 0;
   return gptq::prepare_workspace(d);

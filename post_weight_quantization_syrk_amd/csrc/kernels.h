@@ -19,6 +19,13 @@ struct SyrkPlan {
   size_t ws_bytes;      // = partial_bytes
 };
 SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype);
+// The allocation-free entry point: its split-K partials live in a fixed
+// per-device array of NOALLOC_SCRATCH_BYTES; the split count is capped to fit
+// (splits = 0: even one split does not fit).
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+constexpr int MAX_DEVICES = 64;
+SyrkPlan syrk_plan_capped(int64_t d, int64_t n, int x_dtype, size_t max_bytes);
+hipError_t syrk_scratch(void** ptr);  // this device's copy of the array
 hipError_t syrk_launch(float* H, int64_t d, const void* X, int x_dtype, int64_t n, int64_t ldx,
                        void* ws, const SyrkPlan& plan, hipStream_t stream);
 

@@ -19,6 +19,7 @@
 #include "mfma_f32.h"
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <cmath>
 #include <cstdlib>
@@ -636,6 +637,49 @@ static int pick_splits(int64_t n, int ntri, int stage, double partial_cost) {
     }
   }
   return best;
+}
+
+// ---- the allocation-free entry point's scratch ------------------------------
+// A fixed array in the code object: each GPU the library runs on holds its own
+// copy from the library's load until the process ends.  In host code the
+// name is only a stand-in; the device address comes from hipGetSymbolAddress,
+// taken once per device (with that device current) and kept here.
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+hipError_t syrk_scratch(void** ptr) {
+  static std::mutex mu;
+  static void* cached[MAX_DEVICES] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cached[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    cached[dev] = p;
+  }
+  *ptr = cached[dev];
+  return hipSuccess;
+}
+
+SyrkPlan syrk_plan_capped(int64_t d, int64_t n, int x_dtype, size_t max_bytes) {
+  SyrkPlan p = syrk_plan(d, n, x_dtype);
+  const size_t per_split = (size_t)p.ntri * (size_t)p.tile * p.tile * sizeof(float);
+  const int64_t fit = (int64_t)(max_bytes / per_split);
+  if (fit < 1) {
+    p.splits = 0;  // does not fit even one split
+    return p;
+  }
+  if (p.splits > fit) {
+    const int bk = (x_dtype == 0) ? ABK : BKF;
+    p.splits = (int)fit;
+    p.kper = std::max<int64_t>(bk, ceil_div(ceil_div(std::max<int64_t>(n, 1), p.splits), bk) * bk);
+    p.partial_bytes = (p.splits * per_split + 255) & ~(size_t)255;
+    p.ws_bytes = p.partial_bytes;
+  }
+  return p;
 }
 
 SyrkPlan syrk_plan(int64_t d, int64_t n, int x_dtype) {

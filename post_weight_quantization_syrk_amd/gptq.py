@@ -61,6 +61,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "gptq_hessian_accumulate": (I, [P, I64, P, I, I64, I64, P, SZ, P]),
         "gptq_hessian_workspace": (SZ, [I64, I64, I]),
+        "gptq_hessian_accumulate_noalloc": (I, [P, I64, P, I, I64, I64, P]),
+        "gptq_noalloc_scratch_bytes": (SZ, []),
         "gptq_prepare_hinv": (I, [P, I64, D, P, P, P, P, SZ, P]),
         "gptq_prepare_workspace": (SZ, [I64]),
         "gptq_quantize_layer": (I, [P, I, I64, I64, P, P, I, I, I, I, P, P, P, P, P, SZ, P]),
@@ -141,6 +143,24 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: torch.Tensor |
     _check(lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), xd, n, X.stride(0), _ptr(ws),
                                          nbytes, _stream(stream)), "gptq_hessian_accumulate")
     return H
+
+
+def gptq_hessian_accumulate_noalloc(H: torch.Tensor, X: torch.Tensor, stream=None) -> torch.Tensor:
+    """H (lower triangle) += 2 X^T X with the library's fixed per-GPU scratch: no
+    device memory is allocated by this call (nor by the library)."""
+    d = H.shape[0]
+    if X.dim() != 2 or X.stride(1) != 1 or H.dtype != torch.float32 or not H.is_contiguous():
+        raise ValueError("H must be contiguous fp32 [d, d]; X a row-major [n, >=d] matrix")
+    if X.shape[1] < d:
+        raise ValueError("X has fewer columns than d")
+    _check(lib().gptq_hessian_accumulate_noalloc(_ptr(H), d, _ptr(X), _dtype_code(X), X.shape[0],
+                                                 X.stride(0), _stream(stream)),
+           "gptq_hessian_accumulate_noalloc")
+    return H
+
+
+def gptq_noalloc_scratch_bytes() -> int:
+    return int(lib().gptq_noalloc_scratch_bytes())
 
 
 def gptq_prepare_workspace(d: int) -> int:
