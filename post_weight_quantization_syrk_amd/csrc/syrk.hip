@@ -453,8 +453,16 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
   // immediates on precomputed per-lane bases.
   const int nfull = full_tile ? (int)((ke - kb) / ABK) : 0;
   const bool fast = full_tile && (int64_t)(ABK * a.ldx + a.d) * 2 < ((int64_t)1 << 31);
-  auto fast_loop = [&](auto DiagC) __attribute__((always_inline)) {
+  auto fast_loop = [&](auto DiagC, auto ModeC) __attribute__((always_inline)) {
     constexpr bool DIAG = decltype(DiagC)::value;
+    // Which of the wave's 32 x 32 blocks it multiplies: 0 every block; in a
+    // diagonal tile, 1 for the two quadrants on the diagonal (blocks with
+    // ni <= mi, the rest lie above it) and 2 for the quadrant above the
+    // diagonal (none: the wave only loads and keeps the barriers).  The
+    // blocks left out lie strictly above the diagonal, which the reduction
+    // never reads; under sustained matrix-core load the engine clock is
+    // power-limited, so products saved there speed up the rest.
+    constexpr int MODE = decltype(ModeC)::value;
     constexpr uint32_t OPB = DIAG ? 0u : (uint32_t)AOP;
     // per-lane LDS read bases of slot 1 (stage 1 is read during step 0);
     // moved to the next slot after every step
@@ -494,6 +502,7 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
             dma16_imm<(uint32_t)(SLOT * ASTAGE + AOP + 2 * g * AROW)>(sb, offB.v[g & 1] + ro,
                                                                        ldsw);
           __builtin_amdgcn_sched_barrier(0);
+          if constexpr (MODE != 2) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if constexpr ((g & 1) == 0)
@@ -505,8 +514,10 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
           for (int mi = 2 * (g & 1); mi < 2 * (g & 1) + 2; ++mi)
 #pragma unroll
             for (int ni = 0; ni < 4; ++ni)
-              acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][mi], cur.b[kk][ni],
-                                                                   acc[mi][ni], 0, 0, 0);
+              if (MODE == 0 || ni <= mi)
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur.a[kk][mi], cur.b[kk][ni],
+                                                                     acc[mi][ni], 0, 0, 0);
+          }
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
@@ -529,10 +540,14 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
     }
   };
   if (fast && nst > 0) {
-    if (diag)
-      fast_loop(std::true_type{});
+    if (!diag)
+      fast_loop(std::false_type{}, std::integral_constant<int, 0>{});
+    else if (wm == wn)
+      fast_loop(std::true_type{}, std::integral_constant<int, 1>{});
+    else if (wm < wn)
+      fast_loop(std::true_type{}, std::integral_constant<int, 2>{});
     else
-      fast_loop(std::false_type{});
+      fast_loop(std::true_type{}, std::integral_constant<int, 0>{});
   }
   for (; s + 1 < nst; s += 2) {
     step(s, f0, f1);
