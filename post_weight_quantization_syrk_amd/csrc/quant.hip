@@ -35,16 +35,32 @@ constexpr int QG = 4;        // blocks per far trailing update
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Workspace: the fp32 working copy, then the trailing update's operands
+// split into three bf16 parts (h, m, l): the scaled errors delta and U
+// transposed (row n holds column n of U), both k-chunk major,
+//   E3 [k / 32][part][d_out rows][32],   Ut3 [k / 32][part][d_in rows][32],
+// so the 32 k of one chunk and part are 64 contiguous bytes per row and the
+// rows of a tile follow each other: one tile operand per chunk and part is
+// one contiguous run.
+constexpr int KC = 32;  // k per chunk of the split operands
+
 struct QuantWs {
-  float* Wc;   // [d_out x d_in] working copy
-  float* Err;  // [d_out x d_in] scaled errors delta
+  float* Wc;      // [d_out x d_in] working copy
+  uint16_t* E3;   // parts of the scaled errors delta
+  uint16_t* Ut3;  // parts of U^T (entries with k < n are used)
+  int64_t se, su; // elements per (chunk, part): d_out * KC and d_in * KC
 };
+
+inline int64_t n_chunks(int64_t d_in) { return (d_in + KC - 1) / KC; }
 
 QuantWs carve(void* ws, int64_t d_out, int64_t d_in) {
   QuantWs w;
   const size_t m = align256((size_t)d_out * d_in * sizeof(float));
+  w.se = d_out * KC;
+  w.su = d_in * KC;
   w.Wc = (float*)ws;
-  w.Err = (float*)((char*)ws + m);
+  w.E3 = (uint16_t*)((char*)ws + m);
+  w.Ut3 = (uint16_t*)((char*)w.E3 + align256((size_t)n_chunks(d_in) * 3 * w.se * 2));
   return w;
 }
 
@@ -293,6 +309,41 @@ __device__ __forceinline__ float row_sum(float v) {
   return v;
 }
 
+// Exact three-part bf16 split of fp32 values for the trailing update: x = h
+// + m + l with h the nearest bf16 of x, m that of x - h and l that of the
+// remainder, which has at most 8 significant bits left and so is exact.
+__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
+  const uint32_t b = __float_as_uint(x);
+  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
+  return __uint_as_float((uint32_t)h << 16);
+}
+// The three-part split of one float (element-wise staging).
+__device__ __forceinline__ uint16_t split3(float x, uint16_t& mid, uint16_t& lo) {
+  const uint16_t hi = bf16_rne_bits(x);
+  const float r = x - bf16_bits_to_f32(hi);
+  mid = bf16_rne_bits(r);
+  lo = bf16_rne_bits(r - bf16_bits_to_f32(mid));
+  return hi;
+}
+// The same split for a pair, with the hardware's nearest-even conversion of
+// two floats at once: each part packed low-first into one word.
+typedef float f32x2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ f32x2v bf16x2_widen(uint32_t b) {
+  const f32x2v v = {__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)};
+  return v;
+}
+__device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& mid, uint32_t& lo) {
+  const f32x2v x = {x0, x1};
+  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
+  const f32x2v r = x - bf16x2_widen(hb);
+  mid = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r - bf16x2_widen(mid), bf16x2v));
+  return hb;
+}
+
 // STATIC: the group parameters are given (static groups, natural groups of
 // the original weights, in scales/zeros) and column k of the block uses those
 // of group perm[b0 + k] >> gshift (perm may be null: natural order); they are
@@ -301,7 +352,7 @@ __device__ __forceinline__ float row_sum(float v) {
 // written to scales/zeros.
 template <bool STATIC>
 __global__ __launch_bounds__(256) void colloop_kernel(
-    float* __restrict__ Wc, float* __restrict__ Err, const float* __restrict__ U,
+    float* __restrict__ Wc, uint16_t* __restrict__ E3, int64_t se, const float* __restrict__ U,
     int64_t d_out, int64_t d_in, int64_t b0, QSpec q, uint8_t* __restrict__ codes,
     float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows,
     const int32_t* __restrict__ perm) {
@@ -469,13 +520,13 @@ __global__ __launch_bounds__(256) void colloop_kernel(
   }
   loss = row_sum(loss);
   if (!live) return;
-  // codes and scaled errors of this lane's 8 columns (the errors as two
-  // 16-byte stores when the lane's columns are all inside and 16-byte aligned:
-  // d_in a multiple of 4, b0 a multiple of 128)
-  // (the codes as one 8-byte store when d_in is a multiple of 8 and codes is
-  // 8-byte aligned)
+  // codes and scaled errors of this lane's 8 columns: the codes as one
+  // 8-byte store when d_in is a multiple of 8 and codes is 8-byte aligned;
+  // the errors split into their three bf16 parts, each part's 8 values one
+  // 16-byte store (they lie in one k chunk: b0 and 8 c are multiples of 8)
   uint8_t* cdst = codes + rr * d_in + b0 + 8 * c;
-  float* edst = Err + rr * d_in + b0 + 8 * c;
+  const int64_t kabs = b0 + 8 * c;
+  uint16_t* edst = E3 + (kabs / KC) * 3 * se + rr * KC + kabs % KC;
   if ((d_in & 7) == 0 && ((uintptr_t)codes & 7) == 0 && 8 * c + 8 <= bw) {
     uint32_t cw[2];
 #pragma unroll
@@ -488,83 +539,99 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     for (int i = 0; i < 8; ++i)
       if (8 * c + i < bw) cdst[i] = (uint8_t)cr[i];
   }
-  if ((d_in & 3) == 0 && 8 * c + 8 <= bw) {
-    ((float4*)edst)[0] = make_float4(er[0], er[1], er[2], er[3]);
-    ((float4*)edst)[1] = make_float4(er[4], er[5], er[6], er[7]);
+  if (8 * c + 8 <= bw) {
+    uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) hw[t] = split_pair(er[2 * t], er[2 * t + 1], mw[t], lw[t]);
+    *(uint4*)edst = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(edst + se) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    *(uint4*)(edst + 2 * se) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      if (8 * c + i < bw) edst[i] = er[i];
+      if (8 * c + i < bw) {
+        uint16_t mi, lo;
+        edst[i] = split3(er[i], mi, lo);
+        edst[se + i] = mi;
+        edst[2 * se + i] = lo;
+      }
   }
   if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
 }
 
-// Wc[:, n0:n1] -= Err[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
-// cores.  Each fp32 operand x is split exactly into three bf16 parts, x = h +
-// m + l (h the nearest bf16 of x, m that of x - h, l that of the remainder,
-// which has at most 8 significant bits left and so is exact), and the product
-// is formed from the six part products that matter,
+// Wc[:, n0:n1] -= delta[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
+// cores.  Both operands come already split into their three bf16 parts (the
+// column loop splits the errors it writes, split_ut_kernel splits U^T once
+// per call), and the product is formed from the six part products that
+// matter,
 //   l*h + h*l + m*m + m*h + h*m + h*h,
 // with v_mfma_f32_32x32x16_bf16 into fp32 accumulators, smallest first.  The
 // dropped terms (m*l, l*m, l*l) come to at most about 2^-23 of the product
 // (|m| <= 2^-8 |x|, |l| <= 2^-16 |x|), so each product carries an error of
-// about one fp32 rounding, as with fp32 FMAs; the
-// feedback is then as exact as fp32 working weights allow.  TM x 64 tiles, K
-// in chunks of 32 (two MFMA steps of 16).  The error tile is stored row-major
-// (k contiguous), the U tile transposed (n-major, k contiguous), so every lane
-// reads its 8 consecutive k as 16 bytes; row pitches of 80 bytes keep those
-// reads free of bank conflicts.  The accumulators start at zero and collect
-// Err U, and Wc - acc is stored: summed onto a preloaded Wc instead, every one
-// of the K roundings would be at the weights' magnitude rather than the
-// products'.
-constexpr int T3K = 32;           // k per chunk
+// about one fp32 rounding, as with fp32 FMAs; the feedback is then as exact
+// as fp32 working weights allow.  TM x 64 tiles, K in chunks of 32 (two MFMA
+// steps of 16): a chunk of one part is one contiguous run of the k-chunk
+// major operands, loaded 16 bytes per lane.  Both LDS tiles are k-contiguous
+// rows (the error rows and the rows of U^T), so every lane reads its 8
+// consecutive k as 16 bytes; row pitches of 80 bytes keep those reads free of
+// bank conflicts.  The accumulators start at zero and collect delta U, and Wc
+// - acc is stored: summed onto a preloaded Wc instead, every one of the K
+// roundings would be at the weights' magnitude rather than the products'.
+constexpr int T3K = KC;           // k per chunk
 constexpr int T3P = T3K + 8;      // LDS row pitch (bf16 elements): 80 bytes
 
-__device__ __forceinline__ uint16_t bf16_rne_bits(float x) {
-  const uint32_t b = __float_as_uint(x);
-  return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
-}
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t h) {
-  return __uint_as_float((uint32_t)h << 16);
-}
-// The three-part split of one float (element-wise staging).
-__device__ __forceinline__ uint16_t split3(float x, uint16_t& mid, uint16_t& lo) {
-  const uint16_t hi = bf16_rne_bits(x);
-  const float r = x - bf16_bits_to_f32(hi);
-  mid = bf16_rne_bits(r);
-  lo = bf16_rne_bits(r - bf16_bits_to_f32(mid));
-  return hi;
-}
-// The same split for a pair, with the hardware's nearest-even conversion of
-// two floats at once: each part packed low-first into one word.
-typedef float f32x2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ f32x2v bf16x2_widen(uint32_t b) {
-  const f32x2v v = {__uint_as_float(b << 16), __uint_as_float(b & 0xffff0000u)};
-  return v;
-}
-__device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& mid, uint32_t& lo) {
-  const f32x2v x = {x0, x1};
-  const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2v));
-  const f32x2v r = x - bf16x2_widen(hb);
-  mid = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
-  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r - bf16x2_widen(mid), bf16x2v));
-  return hb;
+// U^T split into parts: part p of U[k][n] goes to Ut3 at chunk k / 32, part
+// p, row n, position k % 32, for the 64 x 64 tiles (k block kt, n block nt)
+// with kt <= nt (the update reads k < n only).  The tile goes through LDS so
+// that the loads of U's rows and the stores of U^T's rows are contiguous.
+__global__ __launch_bounds__(256) void split_ut_kernel(const float* __restrict__ U, int64_t d_in,
+                                                       uint16_t* __restrict__ Ut3, int64_t su) {
+  __shared__ float t[64][65];
+  int nt = (int)((sqrtf(8.0f * (float)blockIdx.x + 1.0f) - 1.0f) * 0.5f);
+  while ((nt + 1) * (nt + 2) / 2 <= (int)blockIdx.x) ++nt;
+  while (nt * (nt + 1) / 2 > (int)blockIdx.x) --nt;
+  const int kt = (int)blockIdx.x - nt * (nt + 1) / 2;
+  const int64_t k0 = 64 * (int64_t)kt, n0 = 64 * (int64_t)nt;
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;  // r = k, c = n
+    const int64_t k = k0 + r, n = n0 + c;
+    t[r][c] = (k < d_in && n < d_in) ? U[k * d_in + n] : 0.0f;
+  }
+  __syncthreads();
+  // thread: row n = tid % 64 of U^T, 16 consecutive k from 16 (tid / 64)
+  // (a wave's stores of one part are 64 rows x 32 bytes of one chunk)
+  const int nl = tid & 63, kl = 16 * (tid >> 6);
+  const int64_t n = n0 + nl;
+  if (n >= d_in || k0 + kl >= d_in) return;
+  uint16_t* dst = Ut3 + ((k0 + kl) / KC) * 3 * su + n * KC + (k0 + kl) % KC;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      hw[q] = split_pair(t[kl + 8 * h + 2 * q][nl], t[kl + 8 * h + 2 * q + 1][nl], mw[q], lw[q]);
+    *(uint4*)(dst + 8 * h) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+    *(uint4*)(dst + su + 8 * h) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+    *(uint4*)(dst + 2 * su + 8 * h) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+  }
 }
 
-// VEC (d_in a multiple of 4, U 16-byte aligned; the launches give kb a
-// multiple of 32 and b0, n0 multiples of 64): each thread loads 4 consecutive
-// k of an error row and 2 k rows x 4 columns of U as 16-byte vectors, and
-// splits and stores them in pairs of k.
-template <int TM, bool VEC>
+// The launches give b0 and kb multiples of 32 (whole chunks) and n0 a
+// multiple of 64; rows past d_out and columns past n1 are loaded as clamped
+// copies of finite values, which only reach accumulator rows or columns that
+// are never stored.
+template <int TM>
 __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
-                                                        const float* __restrict__ Err,
-                                                        const float* __restrict__ U,
-                                                        int64_t d_out, int64_t d_in, int64_t b0,
-                                                        int kb, int64_t n0, int64_t n1) {
+                                                        const uint16_t* __restrict__ E3, int64_t se,
+                                                        const uint16_t* __restrict__ Ut3,
+                                                        int64_t su, int64_t d_out, int64_t d_in,
+                                                        int64_t b0, int kb, int64_t n0,
+                                                        int64_t n1) {
   constexpr int TN = 64;
   constexpr int NBLK = (TM / 32) * (TN / 32) / 4;  // 32 x 32 blocks per wave
-  constexpr int NP = TM * T3K / 256, NQ = T3K * TN / 256;
+  constexpr int VP = TM * T3K / 8 / 256;           // 16-byte pieces per thread and part
+  static_assert(VP >= 1 && TN * T3K / 8 == 256, "one U^T piece per thread and part");
   __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], amid[TM * T3P], al[TM * T3P];
   __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bmid[TN * T3P], bl[TN * T3P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -589,82 +656,52 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
   for (int q = 0; q < NBLK; ++q)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[q][i] = 0.0f;
-  const float* P = Err + m0 * d_in + b0;
-  const float* Q = U + b0 * d_in + n0t;
-  float vp[NP], vq[NQ];
-  static_assert(NQ == 8 && NP % 4 == 0, "vector staging takes 2 x 4 U values per thread");
-  const int vn = 4 * (tid & 15), vk = 2 * (tid >> 4);  // VEC: this thread's U columns, k pair
+  // this thread's pieces: tile row r (clamped), k offset 8 (e % 4)
+  int64_t offp[VP];
+#pragma unroll
+  for (int j = 0; j < VP; ++j) {
+    const int e = j * 256 + tid, r = e >> 2;
+    offp[j] = (m0 + (r < rows ? r : rows - 1)) * KC + 8 * (e & 3);
+  }
+  const int nr = tid >> 2;
+  const int64_t offq = (n0t + (nr < cols ? nr : cols - 1)) * KC + 8 * (tid & 3);
+  // staged chunk, as 32-bit words (arrays of scalars stay in registers)
+  uint32_t xp[3 * VP * 4], xq[3 * 4];
   auto gload = [&](int kc) __attribute__((always_inline)) {
-    const int kn = min(T3K, kb - kc);
-    if constexpr (VEC) {
+    const int64_t ck = (b0 + kc) / KC;
+    const uint16_t* pa = E3 + ck * 3 * se;
+    const uint16_t* pb = Ut3 + ck * 3 * su;
 #pragma unroll
-      for (int j = 0; j < NP / 4; ++j) {
-        const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
-        const float4 v =
-            *(const float4*)(P + (int64_t)(r < rows ? r : rows - 1) * d_in + kc + c);
-        vp[4 * j] = v.x; vp[4 * j + 1] = v.y; vp[4 * j + 2] = v.z; vp[4 * j + 3] = v.w;
+    for (int pt = 0; pt < 3; ++pt) {
+#pragma unroll
+      for (int j = 0; j < VP; ++j) {
+        const uint4 v = *(const uint4*)(pa + pt * se + offp[j]);
+        xp[4 * (3 * j + pt)] = v.x;
+        xp[4 * (3 * j + pt) + 1] = v.y;
+        xp[4 * (3 * j + pt) + 2] = v.z;
+        xp[4 * (3 * j + pt) + 3] = v.w;
       }
-      const int nc = vn < cols ? vn : 0;
-      const float4 v0 = *(const float4*)(Q + (int64_t)(kc + vk) * d_in + nc);
-      const float4 v1 = *(const float4*)(Q + (int64_t)(kc + vk + 1) * d_in + nc);
-      vq[0] = v0.x; vq[1] = v0.y; vq[2] = v0.z; vq[3] = v0.w;
-      vq[4] = v1.x; vq[5] = v1.y; vq[6] = v1.z; vq[7] = v1.w;
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
-      vp[u] = P[(int64_t)(r < rows ? r : rows - 1) * d_in + kc + (c < kn ? c : kn - 1)];
-    }
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = u * 256 + tid, r = e / TN, c = e % TN;
-      vq[u] = Q[(int64_t)(kc + (r < kn ? r : kn - 1)) * d_in + (c < cols ? c : cols - 1)];
+      const uint4 v = *(const uint4*)(pb + pt * su + offq);
+      xq[4 * pt] = v.x;
+      xq[4 * pt + 1] = v.y;
+      xq[4 * pt + 2] = v.z;
+      xq[4 * pt + 3] = v.w;
     }
   };
   auto lstore = [&](int kc) __attribute__((always_inline)) {
-    const int kn = min(T3K, kb - kc);
-    if constexpr (VEC) {
-      // no masks: every k is inside the block, and rows past d_out or columns
-      // past n1 (clamped copies of finite values) only reach accumulator rows
-      // or columns that are never stored
+    (void)kc;
+    uint16_t* const pa[3] = {ah, amid, al};
+    uint16_t* const pb[3] = {bh, bmid, bl};
 #pragma unroll
-      for (int j = 0; j < NP / 4; ++j) {
-        const int e = 4 * (j * 256 + tid), r = e / T3K, c = e % T3K;
-        uint32_t m0, m1, l0, l1;
-        const uint32_t h0 = split_pair(vp[4 * j], vp[4 * j + 1], m0, l0);
-        const uint32_t h1 = split_pair(vp[4 * j + 2], vp[4 * j + 3], m1, l1);
-        *(uint2*)(ah + r * T3P + c) = make_uint2(h0, h1);
-        *(uint2*)(amid + r * T3P + c) = make_uint2(m0, m1);
-        *(uint2*)(al + r * T3P + c) = make_uint2(l0, l1);
+    for (int pt = 0; pt < 3; ++pt) {
+#pragma unroll
+      for (int j = 0; j < VP; ++j) {
+        const int e = j * 256 + tid, r = e >> 2, c = 8 * (e & 3);
+        const int x = 4 * (3 * j + pt);
+        *(uint4*)(pa[pt] + r * T3P + c) = make_uint4(xp[x], xp[x + 1], xp[x + 2], xp[x + 3]);
       }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        uint32_t m, l;
-        const uint32_t hw = split_pair(vq[t], vq[4 + t], m, l);
-        *(uint32_t*)(bh + (vn + t) * T3P + vk) = hw;
-        *(uint32_t*)(bmid + (vn + t) * T3P + vk) = m;
-        *(uint32_t*)(bl + (vn + t) * T3P + vk) = l;
-      }
-      return;
-    }
-#pragma unroll
-    for (int u = 0; u < NP; ++u) {
-      const int e = u * 256 + tid, r = e / T3K, c = e % T3K;
-      const float x = (r < rows && c < kn) ? vp[u] : 0.0f;
-      uint16_t mi, lo;
-      ah[r * T3P + c] = split3(x, mi, lo);
-      amid[r * T3P + c] = mi;
-      al[r * T3P + c] = lo;
-    }
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int e = u * 256 + tid, r = e / TN, c = e % TN;  // r = k, c = n
-      const float x = (r < kn && c < cols) ? vq[u] : 0.0f;
-      uint16_t mi, lo;
-      bh[c * T3P + r] = split3(x, mi, lo);
-      bmid[c * T3P + r] = mi;
-      bl[c * T3P + r] = lo;
+      *(uint4*)(pb[pt] + nr * T3P + 8 * (tid & 3)) =
+          make_uint4(xq[4 * pt], xq[4 * pt + 1], xq[4 * pt + 2], xq[4 * pt + 3]);
     }
   };
   gload(0);
@@ -748,7 +785,10 @@ __global__ __launch_bounds__(256) void pack_meta_kernel(const float* __restrict_
 }  // namespace
 
 size_t quantize_workspace(int64_t d_out, int64_t d_in, int /*block*/) {
-  return 2 * align256((size_t)d_out * d_in * sizeof(float));
+  const size_t per_chunk = 3 * KC * sizeof(uint16_t);  // three parts of 32 k
+  return align256((size_t)d_out * d_in * sizeof(float)) +
+         align256((size_t)n_chunks(d_in) * per_chunk * d_out) +
+         align256((size_t)n_chunks(d_in) * per_chunk * d_in);
 }
 
 size_t quantize_perm_workspace(int64_t d_out, int64_t d_in, int block) {
@@ -823,7 +863,13 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // K = 128 QG), so the bulk of W is read and written once per group.
   const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
   static_assert(QB % T3K == 0, "trailing updates take whole chunks");
-  const bool tvec = (d_in % 4 == 0) && ((uintptr_t)U % 16 == 0);
+  // U^T in parts, for every trailing update of this call (only the 64 x 64
+  // tiles on or above U's diagonal)
+  if (d_in > QB) {
+    const int64_t nt = ceil_div(d_in, 64);
+    hipLaunchKernelGGL(split_ut_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, stream,
+                       U, d_in, w.Ut3, w.su);
+  }
   const int64_t nb = ceil_div(d_in, QB);
   for (int64_t g0 = 0; g0 < nb; g0 += QG) {
     const int64_t gend = std::min<int64_t>(nb, g0 + QG);
@@ -831,33 +877,25 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
     for (int64_t b = g0; b < gend; ++b) {
       const int64_t b0 = b * QB;
       if (stat)
-        hipLaunchKernelGGL(colloop_kernel<true>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err,
-                           U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
+        hipLaunchKernelGGL(colloop_kernel<true>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.E3,
+                           w.se, U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
       else
-        hipLaunchKernelGGL(colloop_kernel<false>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.Err,
-                           U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
+        hipLaunchKernelGGL(colloop_kernel<false>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.E3,
+                           w.se, U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        if (tvec)
-          hipLaunchKernelGGL((trailing3_kernel<64, true>), dim3((unsigned)tiles), dim3(256), 0,
-                             stream, w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
-        else
-          hipLaunchKernelGGL((trailing3_kernel<64, false>), dim3((unsigned)tiles), dim3(256), 0,
-                             stream, w.Wc, (const float*)w.Err, U, d_out, d_in, b0, QB, n0, gcol);
+        hipLaunchKernelGGL((trailing3_kernel<64>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                           w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
+                           d_in, b0, QB, n0, gcol);
       }
     }
     if (gcol < d_in) {  // every block of the group is full
       const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
       const int kb = (int)(gcol - g0 * QB);
-      if (tvec)
-        hipLaunchKernelGGL((trailing3_kernel<128, true>), dim3((unsigned)tiles), dim3(256), 0,
-                           stream, w.Wc, (const float*)w.Err, U, d_out, d_in, g0 * QB, kb, gcol,
-                           d_in);
-      else
-        hipLaunchKernelGGL((trailing3_kernel<128, false>), dim3((unsigned)tiles), dim3(256), 0,
-                           stream, w.Wc, (const float*)w.Err, U, d_out, d_in, g0 * QB, kb, gcol,
-                           d_in);
+      hipLaunchKernelGGL((trailing3_kernel<128>), dim3((unsigned)tiles), dim3(256), 0, stream,
+                         w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
+                         d_in, g0 * QB, kb, gcol, d_in);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
