@@ -32,6 +32,7 @@ namespace {
 constexpr int QB = 128;      // block width (columns)
 constexpr int UPITCH = 132;  // LDS pitch (floats) of the U block in the column loop
 constexpr int QG = 4;        // blocks per far trailing update
+constexpr int CL_LPR = 16;   // lanes per row in the column loop
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -44,14 +45,19 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // one contiguous run.
 constexpr int KC = 32;  // k per chunk of the split operands
 
+// Then the column loop's diagonal blocks of U: block b's rows scaled by
+// 1 / U_jj (Ub, [blocks][QB][QB]) and the 1 / U_jj themselves (Uinv).
 struct QuantWs {
   float* Wc;      // [d_out x d_in] working copy
   uint16_t* E3;   // parts of the scaled errors delta
   uint16_t* Ut3;  // parts of U^T (entries with k < n are used)
+  float* Ub;      // scaled diagonal blocks of U
+  float* Uinv;    // 1 / U_jj
   int64_t se, su; // elements per (chunk, part): d_out * KC and d_in * KC
 };
 
 inline int64_t n_chunks(int64_t d_in) { return (d_in + KC - 1) / KC; }
+inline int64_t n_blocks(int64_t d_in) { return (d_in + QB - 1) / QB; }
 
 QuantWs carve(void* ws, int64_t d_out, int64_t d_in) {
   QuantWs w;
@@ -61,6 +67,8 @@ QuantWs carve(void* ws, int64_t d_out, int64_t d_in) {
   w.Wc = (float*)ws;
   w.E3 = (uint16_t*)((char*)ws + m);
   w.Ut3 = (uint16_t*)((char*)w.E3 + align256((size_t)n_chunks(d_in) * 3 * w.se * 2));
+  w.Ub = (float*)((char*)w.Ut3 + align256((size_t)n_chunks(d_in) * 3 * w.su * 2));
+  w.Uinv = w.Ub + n_blocks(d_in) * QB * QB;
   return w;
 }
 
@@ -184,7 +192,8 @@ __global__ __launch_bounds__(256) void gidx_kernel(const int32_t* __restrict__ p
 
 struct GroupParams {
   float s, inv_s, hs, z;
-  float hs_lo;  // the largest float below hs (s/2)
+  float hs_lo;     // the largest float below hs (s/2)
+  float zlo, zhi;  // -z and maxq - z: the range of code - z
 };
 
 // Scale and zero from the group's min/max (asymmetric) or max |v| (symmetric).
@@ -215,22 +224,35 @@ __device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi, i
   p.hs = 0.5f * p.s;
   p.hs_lo = __int_as_float(__float_as_int(p.hs) - 1);  // hs >= 2^-25: a normal float
   p.z = z;
+  p.zlo = -z;
+  p.zhi = (float)maxq - z;
   return p;
 }
 
 // Nearest integer to the exact quotient x/s, ties to even, then code clamp.
-// q0 = rint(x * (1/s)) is within 1 of it.  r = x - q0 s is exact (q0 s has
-// at most 22 significant bits, and |r| <= s keeps the difference within
-// x's precision), so comparing r with +-s/2 settles the last unit; a tie
-// (|r| = s/2) moves an odd q0 to its even neighbour, which is the same as
-// comparing against the float just below s/2 when q0 is odd.  Selects only:
-// this sits on the column loop's dependency chain.
-__device__ __forceinline__ float quantize_code(float x, const GroupParams& p, float maxq) {
-  const float q0 = __builtin_amdgcn_fmed3f(rintf(x * p.inv_s), -2047.0f, 2047.0f);
-  const float t = (((int)q0) & 1) ? p.hs_lo : p.hs;
+// q0, the nearest integer to y = x * (1/s), is within 1 of it: adding 1.5 *
+// 2^23 to y rounds y half-to-even into the sum's last mantissa bit (for |y| <
+// 2^22, where that sum has unit spacing), which then holds q0's parity, and
+// subtracting it again gives q0 exactly.  r = x - q0 s is exact (q0 s has at
+// most 22 significant bits while |q0| <= 2^11, and |r| <= s keeps the
+// difference within x's precision), so comparing r with +-s/2 settles the
+// last unit; a tie (|r| = s/2) moves an odd q0 to its even neighbour, which
+// is the same as comparing against the float just below s/2 when q0 is odd.
+// Larger |y| (where r may be inexact) clamp to 0 or maxq whatever the last
+// unit.  The clamp is applied to code - z (to [-z, maxq - z], exact on these
+// small integers), and the error x - s (code - z) is formed with one
+// rounding.  Selects only: this sits on the column loop's dependency chain.
+// Returns the error; the code goes to *code.
+__device__ __forceinline__ float quantize_step(float x, const GroupParams& p, float* code) {
+  constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
+  const float m = fmaf(x, p.inv_s, MAGIC);
+  const float q0 = m - MAGIC;
+  const float t = (__float_as_uint(m) & 1u) ? p.hs_lo : p.hs;
   const float r = fmaf(-q0, p.s, x);
-  const float adj = (r > t) ? 1.0f : ((r < -t) ? -1.0f : 0.0f);
-  return __builtin_amdgcn_fmed3f(q0 + adj + p.z, 0.0f, maxq);
+  const float v = (r > t) ? q0 + 1.0f : ((r < -t) ? q0 - 1.0f : q0);
+  const float cz = __builtin_amdgcn_fmed3f(v, p.zlo, p.zhi);
+  *code = cz + p.z;
+  return fmaf(-p.s, cz, x);
 }
 
 // One group per row: parameters from the whole (current = original) row.
@@ -293,20 +315,40 @@ __global__ __launch_bounds__(256) void static_params_kernel(const void* __restri
   }
 }
 
+// Reductions over the LPR lanes that share one row.
+template <int LPR>
 __device__ __forceinline__ float row_min(float v) {
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fminf(v, __shfl_xor(v, m, 16));
+  for (int m = 1; m < LPR; m <<= 1) v = fminf(v, __shfl_xor(v, m, LPR));
   return v;
 }
+template <int LPR>
 __device__ __forceinline__ float row_max(float v) {
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
+  for (int m = 1; m < LPR; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, LPR));
   return v;
 }
+template <int LPR>
 __device__ __forceinline__ float row_sum(float v) {
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) v += __shfl_xor(v, m, 16);
+  for (int m = 1; m < LPR; m <<= 1) v += __shfl_xor(v, m, LPR);
   return v;
+}
+// Lane SRC's v to every lane of its LPR-lane row group (LPR = 16: one DPP
+// row broadcast; LPR = 32: the broadcast inside each 16-lane row, then
+// v_permlane16_swap, which hands each odd row the even row's value and each
+// even row the odd row's, so that both halves of the group see the owner's).
+template <int LPR, int SRC>
+__device__ __forceinline__ float group_bcast(float v) {
+  const float r = row_bcast<(SRC & 15)>(v);
+  if constexpr (LPR == 16) {
+    return r;
+  } else {
+    static_assert(LPR == 32, "16 or 32 lanes per row");
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(r), __float_as_uint(r),
+                                                     false, false);
+    return __uint_as_float(SRC < 16 ? pr[0] : pr[1]);
+  }
 }
 
 // Exact three-part bf16 split of fp32 values for the trailing update: x = h
@@ -344,56 +386,86 @@ __device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& mid
   return hb;
 }
 
+// The column loop's diagonal blocks of U, once per call: block b (columns
+// b0 = QB b ..) as its upper triangle with identity padding past the matrix
+// edge, row j scaled by 1 / U_jj, and the 1 / U_jj.  Column j's feedback is
+// then its unscaled error x - what times the scaled row, and neither the
+// division nor its read sits on the chain from one column to the next.  One
+// workgroup per block; thread t does half t % 2 of row t / 2.
+__global__ __launch_bounds__(256) void ublock_kernel(const float* __restrict__ U, int64_t d_in,
+                                                     float* __restrict__ Ub,
+                                                     float* __restrict__ Uinv) {
+  const int64_t b0 = (int64_t)blockIdx.x * QB;
+  const int bw = (int)min<int64_t>(QB, d_in - b0);
+  const int tid = threadIdx.x, r = tid >> 1, h = tid & 1;
+  const float diag = (r < bw) ? U[(b0 + r) * d_in + b0 + r] : 1.0f;
+  const float sc = 1.0f / diag;
+  if (h == 0) Uinv[b0 + r] = sc;
+  float* dst = Ub + (int64_t)blockIdx.x * QB * QB + r * QB + 64 * h;
+  const float* src = U + (b0 + min(r, bw - 1)) * d_in + b0;
+#pragma unroll 4
+  for (int i = 0; i < 64; ++i) {
+    const int cc = 64 * h + i;
+    const float x = src[min(cc, bw - 1)];  // clamped address, masked below
+    const float v = (r < bw && cc < bw) ? (cc >= r ? x : 0.0f) : (r == cc ? 1.0f : 0.0f);
+    dst[i] = v * sc;
+  }
+}
+
 // STATIC: the group parameters are given (static groups, natural groups of
 // the original weights, in scales/zeros) and column k of the block uses those
 // of group perm[b0 + k] >> gshift (perm may be null: natural order); they are
 // staged in LDS per row and column at the start.  Otherwise each group's
 // parameters are set at its first column from the current values and
 // written to scales/zeros.
-template <bool STATIC>
+template <bool STATIC, int LPR>
 __global__ __launch_bounds__(256) void colloop_kernel(
-    float* __restrict__ Wc, uint16_t* __restrict__ E3, int64_t se, const float* __restrict__ U,
-    int64_t d_out, int64_t d_in, int64_t b0, QSpec q, uint8_t* __restrict__ codes,
+    float* __restrict__ Wc, uint16_t* __restrict__ E3, int64_t se, const float* __restrict__ Ub,
+    const float* __restrict__ Uinv, int64_t d_out, int64_t d_in, int64_t b0, QSpec q,
+    uint8_t* __restrict__ codes,
     float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows,
     const int32_t* __restrict__ perm) {
+  constexpr int CPL = QB / LPR;   // columns per lane
+  constexpr int RPB = 256 / LPR;  // rows per workgroup
+  static_assert(CPL == 4 || CPL == 8, "16 or 32 lanes per row");
   __shared__ __attribute__((aligned(16))) float us[QB * UPITCH];
   __shared__ float invd[QB];
-  __shared__ float sps[STATIC ? 16 * QB : 1], spi[STATIC ? 16 * QB : 1], spz[STATIC ? 16 * QB : 1];
+  __shared__ float sps[STATIC ? RPB * QB : 1], spi[STATIC ? RPB * QB : 1],
+      spz[STATIC ? RPB * QB : 1];
   const int tid = threadIdx.x;
   const int bw = (int)min<int64_t>(QB, d_in - b0);
-  const int c = tid & 15;  // lane within the row group
-  const int64_t row = (int64_t)blockIdx.x * 16 + (tid >> 4);
+  const int c = tid & (LPR - 1);  // lane within the row group
+  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
   const bool live = row < d_out;
   const int64_t rr = live ? row : 0;
   const float maxq = (float)q.maxq;
-  float w[8];
+  float w[CPL];
   {
-    // this lane's 8 columns of the row (unconditional loads, masked after)
+    // this lane's CPL columns of the row (unconditional loads, masked after)
     const float* src = Wc + rr * d_in + b0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = src[min(8 * c + i, bw - 1)];
+    for (int i = 0; i < CPL; ++i) w[i] = src[min(CPL * c + i, bw - 1)];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w[i] = (8 * c + i < bw) ? w[i] : 0.0f;
+    for (int i = 0; i < CPL; ++i) w[i] = (CPL * c + i < bw) ? w[i] : 0.0f;
   }
-  // U block: upper triangle only, identity padding past the matrix edge.
-  // 64 elements per thread, all loads in flight at once (clamped addresses).
+  // this block's diagonal block of U, rows scaled by 1 / U_jj (prepared once
+  // per call), and the 1 / U_jj: 16 float4 per thread
   {
-    float v[QB * QB / 256];
+    const float4* ub = (const float4*)(Ub + (b0 / QB) * QB * QB);
+    float4 v[QB * QB / 4 / 256];
 #pragma unroll
-    for (int u = 0; u < QB * QB / 256; ++u) {
-      const int e = u * 256 + tid, r = e >> 7, cc = e & 127;
-      v[u] = U[(b0 + min(r, bw - 1)) * d_in + b0 + min(cc, bw - 1)];
-    }
+    for (int u = 0; u < QB * QB / 4 / 256; ++u) v[u] = ub[u * 256 + tid];
 #pragma unroll
-    for (int u = 0; u < QB * QB / 256; ++u) {
-      const int e = u * 256 + tid, r = e >> 7, cc = e & 127;
-      us[r * UPITCH + cc] = (r < bw && cc < bw) ? (cc >= r ? v[u] : 0.0f) : (r == cc ? 1.0f : 0.0f);
+    for (int u = 0; u < QB * QB / 4 / 256; ++u) {
+      const int e = u * 256 + tid, r = e / (QB / 4), c4 = e % (QB / 4);
+      *(float4*)(us + r * UPITCH + 4 * c4) = v[u];
     }
+    if (tid < QB) invd[tid] = Uinv[b0 + tid];
   }
   if constexpr (STATIC) {
-    for (int e = tid; e < 16 * QB; e += 256) {
+    for (int e = tid; e < RPB * QB; e += 256) {
       const int rl = e / QB, k = e % QB;
-      const int64_t r = min<int64_t>((int64_t)blockIdx.x * 16 + rl, d_out - 1);
+      const int64_t r = min<int64_t>((int64_t)blockIdx.x * RPB + rl, d_out - 1);
       const int64_t col = b0 + min(k, bw - 1);
       const int64_t pc = perm ? min<int64_t>(max(perm[col], 0), d_in - 1) : col;
       const int64_t gi = r * q.n_groups + (pc >> q.gshift);
@@ -401,26 +473,6 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       sps[e] = sv;
       spi[e] = 1.0f / sv;
       spz[e] = zeros[gi];
-    }
-  }
-  __syncthreads();
-  if (tid < QB) invd[tid] = 1.0f / us[tid * UPITCH + tid];
-  __syncthreads();
-  // Row j of the block scaled by 1 / U_jj: column j's feedback is then its
-  // unscaled error x - what times the scaled row, and neither the division
-  // nor its LDS read sits on the chain from one column to the next.  Thread
-  // t scales half t % 2 of row t / 2 (16-byte LDS accesses).
-  {
-    const float sc = invd[tid >> 1];
-    float4* rw = (float4*)(us + (tid >> 1) * UPITCH + 64 * (tid & 1));
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float4 v = rw[i];
-      v.x *= sc;
-      v.y *= sc;
-      v.z *= sc;
-      v.w *= sc;
-      rw[i] = v;
     }
   }
   __syncthreads();
@@ -432,20 +484,35 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     gp.hs = 0.5f * gp.s;
     gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
     gp.z = zeros[rr];
+    gp.zlo = -gp.z;
+    gp.zhi = maxq - gp.z;
   }
   const int gmask = q.gsize - 1;
   // STATIC: the next column's parameters, read one column ahead
   float ns = 0.0f, ni = 0.0f, nz = 0.0f;
   if constexpr (STATIC) {
-    const int e = (tid >> 4) * QB;
+    const int e = (tid / LPR) * QB;
     ns = sps[e];
     ni = spi[e];
     nz = spz[e];
   }
-  float cr[8], er[8];
-  // U row of the next column, read one column ahead so the LDS latency is off
-  // the dependency chain.
-  float4 un0 = ((const float4*)(us + 8 * c))[0], un1 = ((const float4*)(us + 8 * c))[1];
+  float cr[CPL], er[CPL];
+  // U row of the next column (this lane's CPL entries), read one column
+  // ahead so the LDS latency is off the dependency chain.
+  float un[CPL];
+  auto read_urow = [&](int jn) __attribute__((always_inline)) {
+    const float4* urow = (const float4*)(us + jn * UPITCH + CPL * c);
+#pragma unroll
+    for (int h = 0; h < CPL / 4; ++h) {
+      const float4 v = urow[h];
+      un[4 * h] = v.x;
+      un[4 * h + 1] = v.y;
+      un[4 * h + 2] = v.z;
+      un[4 * h + 3] = v.w;
+    }
+  };
+  read_urow(0);
+  float xv = w[0];
   // Fully unrolled over the 128 columns: register indices and the DPP source
   // lane are compile-time constants.  Columns past the matrix edge (j >= bw)
   // run too, on zero weights against identity rows of U: their delta is 0,
@@ -457,99 +524,111 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       gp.s = ns;
       gp.inv_s = ni;
       gp.z = nz;
+      gp.zlo = -nz;
+      gp.zhi = maxq - nz;
       gp.hs = 0.5f * gp.s;
       gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
       if constexpr (j + 1 < QB) {
-        const int e = (tid >> 4) * QB + j + 1;
+        const int e = (tid / LPR) * QB + j + 1;
         ns = sps[e];
         ni = spi[e];
         nz = spz[e];
       }
     } else if constexpr (j % 32 == 0) {  // every supported group size is a multiple of 32
       if (q.gsize != 0 && (j & gmask) == 0) {
-        const bool mine = (8 * c >= j) && (8 * c < j + q.gsize);
+        const bool mine = (CPL * c >= j) && (CPL * c < j + q.gsize);
         float mn = 0.0f, mx = 0.0f;
         if (mine) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
+          for (int i = 0; i < CPL; ++i) {
             mn = fminf(mn, w[i]);
             mx = fmaxf(mx, q.sym ? fabsf(w[i]) : w[i]);
           }
         }
-        mx = row_max(mx);
-        mn = row_min(mn);
+        mx = row_max<LPR>(mx);
+        mn = row_min<LPR>(mn);
         gp = q.sym ? make_params(mx, 0.0f, q.maxq, 1) : make_params(mn, mx, q.maxq, 0);
-        if (c == (j >> 3) && live && j < bw) {
+        if (c == j / CPL && live && j < bw) {
           const int64_t gi = rr * q.n_groups + ((b0 + j) >> q.gshift);
           scales[gi] = gp.s;
           zeros[gi] = gp.z;
         }
       }
     }
-    const float x = row_bcast<(j >> 3)>(w[j & 7]);
-    const float code = quantize_code(x, gp, maxq);
-    const float what = gp.s * (code - gp.z);
-    const float e = x - what;
-    if (c == (j >> 3)) {
-      cr[j & 7] = code;
-      er[j & 7] = e;
+    // xv: column j's current value on its owner lane (lane j / CPL).  The
+    // owner quantizes it, updates its own next column with its own error, and
+    // so carries the chain from column to column without a broadcast as long
+    // as the next column is its own; the error reaches the other lanes by a
+    // DPP broadcast that only their later columns wait for.
+    float code;
+    const float e = quantize_step(xv, gp, &code);
+    if (c == j / CPL) {
+      cr[j % CPL] = code;
+      er[j % CPL] = e;
     }
-    const float4 u0 = un0, u1 = un1;
-    if constexpr (j + 1 < QB) {
-      const float4* urow = (const float4*)(us + (j + 1) * UPITCH + 8 * c);
-      un0 = urow[0];
-      un1 = urow[1];
-    }
-    w[0] = fmaf(-e, u0.x, w[0]);
-    w[1] = fmaf(-e, u0.y, w[1]);
-    w[2] = fmaf(-e, u0.z, w[2]);
-    w[3] = fmaf(-e, u0.w, w[3]);
-    w[4] = fmaf(-e, u1.x, w[4]);
-    w[5] = fmaf(-e, u1.y, w[5]);
-    w[6] = fmaf(-e, u1.z, w[6]);
-    w[7] = fmaf(-e, u1.w, w[7]);
+    float uu[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) uu[i] = un[i];
+    if constexpr (j + 1 < QB) read_urow(j + 1);
+    constexpr int nx = (j + 1) % CPL;
+    if constexpr (j + 1 < QB && nx != 0) xv = fmaf(-e, uu[nx], w[nx]);
+    // every lane's columns, with the owner's error (the owner's own
+    // broadcast is its e, so its next column gets the value xv holds)
+    const float eb = group_bcast<LPR, j / CPL>(e);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) w[i] = fmaf(-eb, uu[i], w[i]);
+    if constexpr (j + 1 < QB && nx == 0) xv = w[0];  // the next lane's first column
   });
-  // the scaled errors delta = (x - what) / U_jj of this lane's 8 columns
+  // the scaled errors delta = (x - what) / U_jj of this lane's columns
   // (columns past the edge have x - what = 0), and the row's loss sum_j
-  // delta_j^2: this lane's 8 terms, then the row's 16 lanes
+  // delta_j^2: this lane's terms, then the row's lanes
   float loss = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    er[i] *= invd[8 * c + i];
+  for (int i = 0; i < CPL; ++i) {
+    er[i] *= invd[CPL * c + i];
     loss = fmaf(er[i], er[i], loss);
   }
-  loss = row_sum(loss);
+  loss = row_sum<LPR>(loss);
   if (!live) return;
-  // codes and scaled errors of this lane's 8 columns: the codes as one
-  // 8-byte store when d_in is a multiple of 8 and codes is 8-byte aligned;
-  // the errors split into their three bf16 parts, each part's 8 values one
-  // 16-byte store (they lie in one k chunk: b0 and 8 c are multiples of 8)
-  uint8_t* cdst = codes + rr * d_in + b0 + 8 * c;
-  const int64_t kabs = b0 + 8 * c;
+  // codes and scaled errors of this lane's columns: the codes as one store
+  // of CPL bytes when d_in is a multiple of CPL and codes is aligned to it;
+  // the errors split into their three bf16 parts, one store of CPL values per
+  // part (they lie in one k chunk: b0 and CPL c are multiples of CPL)
+  uint8_t* cdst = codes + rr * d_in + b0 + CPL * c;
+  const int64_t kabs = b0 + CPL * c;
   uint16_t* edst = E3 + (kabs / KC) * 3 * se + rr * KC + kabs % KC;
-  if ((d_in & 7) == 0 && ((uintptr_t)codes & 7) == 0 && 8 * c + 8 <= bw) {
-    uint32_t cw[2];
+  if ((d_in % CPL) == 0 && ((uintptr_t)codes % CPL) == 0 && CPL * c + CPL <= bw) {
+    uint32_t cw[CPL / 4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < CPL / 4; ++t)
       cw[t] = (uint32_t)cr[4 * t] | ((uint32_t)cr[4 * t + 1] << 8) |
               ((uint32_t)cr[4 * t + 2] << 16) | ((uint32_t)cr[4 * t + 3] << 24);
-    *(uint2*)cdst = make_uint2(cw[0], cw[1]);
+    if constexpr (CPL == 8)
+      *(uint2*)cdst = make_uint2(cw[0], cw[1]);
+    else
+      *(uint32_t*)cdst = cw[0];
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (8 * c + i < bw) cdst[i] = (uint8_t)cr[i];
+    for (int i = 0; i < CPL; ++i)
+      if (CPL * c + i < bw) cdst[i] = (uint8_t)cr[i];
   }
-  if (8 * c + 8 <= bw) {
-    uint32_t hw[4], mw[4], lw[4];
+  if (CPL * c + CPL <= bw) {
+    uint32_t hw[CPL / 2], mw[CPL / 2], lw[CPL / 2];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) hw[t] = split_pair(er[2 * t], er[2 * t + 1], mw[t], lw[t]);
-    *(uint4*)edst = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-    *(uint4*)(edst + se) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-    *(uint4*)(edst + 2 * se) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    for (int t = 0; t < CPL / 2; ++t) hw[t] = split_pair(er[2 * t], er[2 * t + 1], mw[t], lw[t]);
+    if constexpr (CPL == 8) {
+      *(uint4*)edst = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *(uint4*)(edst + se) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+      *(uint4*)(edst + 2 * se) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    } else {
+      *(uint2*)edst = make_uint2(hw[0], hw[1]);
+      *(uint2*)(edst + se) = make_uint2(mw[0], mw[1]);
+      *(uint2*)(edst + 2 * se) = make_uint2(lw[0], lw[1]);
+    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      if (8 * c + i < bw) {
+    for (int i = 0; i < CPL; ++i)
+      if (CPL * c + i < bw) {
         uint16_t mi, lo;
         edst[i] = split3(er[i], mi, lo);
         edst[se + i] = mi;
@@ -788,7 +867,8 @@ size_t quantize_workspace(int64_t d_out, int64_t d_in, int /*block*/) {
   const size_t per_chunk = 3 * KC * sizeof(uint16_t);  // three parts of 32 k
   return align256((size_t)d_out * d_in * sizeof(float)) +
          align256((size_t)n_chunks(d_in) * per_chunk * d_out) +
-         align256((size_t)n_chunks(d_in) * per_chunk * d_in);
+         align256((size_t)n_chunks(d_in) * per_chunk * d_in) +
+         align256((size_t)n_blocks(d_in) * QB * (QB + 1) * sizeof(float));
 }
 
 size_t quantize_perm_workspace(int64_t d_out, int64_t d_in, int block) {
@@ -861,8 +941,10 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // the rest of its group only (near update, K = 128); after the group, all
   // of the group's errors go to the columns after it at once (far update,
   // K = 128 QG), so the bulk of W is read and written once per group.
-  const unsigned rgrid = (unsigned)ceil_div(d_out, 16);
+  const unsigned rgrid = (unsigned)ceil_div(d_out, 256 / CL_LPR);
   static_assert(QB % T3K == 0, "trailing updates take whole chunks");
+  hipLaunchKernelGGL(ublock_kernel, dim3((unsigned)n_blocks(d_in)), dim3(256), 0, stream, U, d_in,
+                     w.Ub, w.Uinv);
   // U^T in parts, for every trailing update of this call (only the 64 x 64
   // tiles on or above U's diagonal)
   if (d_in > QB) {
@@ -877,11 +959,13 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
     for (int64_t b = g0; b < gend; ++b) {
       const int64_t b0 = b * QB;
       if (stat)
-        hipLaunchKernelGGL(colloop_kernel<true>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.E3,
-                           w.se, U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
+        hipLaunchKernelGGL((colloop_kernel<true, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
+                           w.E3, w.se, w.Ub, w.Uinv, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows,
+                           perm);
       else
-        hipLaunchKernelGGL(colloop_kernel<false>, dim3(rgrid), dim3(256), 0, stream, w.Wc, w.E3,
-                           w.se, U, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows, perm);
+        hipLaunchKernelGGL((colloop_kernel<false, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
+                           w.E3, w.se, w.Ub, w.Uinv, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows,
+                           perm);
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
