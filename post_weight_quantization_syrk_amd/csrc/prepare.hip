@@ -180,6 +180,33 @@ __global__ __launch_bounds__(256) void prep_perm_kernel(const float* __restrict_
 constexpr int SB = 16;
 constexpr int PP16 = 20;  // LDS pitch (floats) of the 16-wide panel copy: 16-byte rows
 
+// DPP row broadcasts fused into the multiply-add that consumes them.  The
+// compiler keeps a v_mov_b32_dpp apart from its v_fmac_f32 (and reuses one
+// temporary for all of them, which serialises the pairs), so the fused form
+// v_fmac_f32_dpp is written out:  acc += (lane SRC of b's 16-lane row) * m.
+// A DPP read of a VGPR needs two wait states after the VALU instruction that
+// wrote it; the inline assembly is opaque to the compiler's hazard checks,
+// so those states are inserted explicitly: dpp_source_ready after the sources
+// of a run of fmac_bcast are computed, and bcast_after_write for a value
+// that an fmac_bcast has just written.
+template <int SRC>
+__device__ __forceinline__ void fmac_bcast(float& acc, float b, float m) {
+  asm volatile("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+               : "+v"(acc)
+               : "v"(b), "v"(m), "n"(SRC));
+}
+__device__ __forceinline__ void dpp_source_ready(float b, float m) {
+  asm volatile("s_nop 1" ::"v"(b), "v"(m));
+}
+template <int SRC>
+__device__ __forceinline__ float bcast_after_write(float v) {
+  float r;
+  asm volatile("s_nop 1\n\tv_mov_b32_dpp %0, %1 row_newbcast:%2 row_mask:0xf bank_mask:0xf"
+               : "=v"(r)
+               : "v"(v), "n"(SRC));
+  return r;
+}
+
 struct DiagLds {
   float tile[NB][NB + 1];   // A_kk, becomes L_kk (lower)
   float mtile[NB][NB + 1];  // L_kk^{-1} (lower)
@@ -256,17 +283,20 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
       float myinv = 0.0f;
       StaticFor<0, SB>::run([&](auto Cv) {
         constexpr int c = decltype(Cv)::value;
-        const float inv = __builtin_amdgcn_rsqf(row_bcast<c>(a[c]));  // 1/sqrt, within 1 ulp
+        const float inv = __builtin_amdgcn_rsqf(bcast_after_write<c>(a[c]));  // 1/sqrt, within 1 ulp
         const float l = a[c] * inv;  // L[r][c] below the pivot, L[c][c] on it
         a[c] = l;
         const float nl = l * ngt[c];  // -L[r][c] below the pivot, 0 elsewhere
+        dpp_source_ready(l, nl);
         StaticFor<c + 1, SB>::run([&](auto Jv) {
           constexpr int j = decltype(Jv)::value;
-          a[j] = fmaf(row_bcast<j>(l), nl, a[j]);
+          fmac_bcast<j>(a[j], l, nl);  // a[j] += L[j][c] nl
         });
         const float nlm = nl * inv;  // -L[r][c] / L[c][c]
+        dpp_source_ready(mv[0], mv[1]);  // (their first values come from plain code)
+        dpp_source_ready(mv[2], mv[3]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) mv[q] = fmaf(row_bcast<c>(mv[q]), nlm, mv[q]);
+        for (int q = 0; q < 4; ++q) fmac_bcast<c>(mv[q], mv[q], nlm);
         myinv = fmaf(inv, eqf[c], myinv);
       });
       if (grp == 0) {
@@ -691,7 +721,10 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
         if (row < ib && col < kb) Arj[(int64_t)row * d + col] = acc[j][q];
       });
     }
-    if (r < nj) publish(fcol + j * NJ + r);
+    // (a panel row block publishes L_rj after its own update below: the
+    // stores complete meanwhile, and the workgroups that wait for it need it
+    // only after the next diagonal block, so the wait for them stays off the
+    // chain of diagonal blocks)
     // later panel columns of this row block: A_{r,jj} -= L_rj L_{jj,j}^T
     StaticFor<j + 1, NJ>::run([&](auto JJ) {
       constexpr int jj = decltype(JJ)::value;
@@ -715,6 +748,7 @@ __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[jj][q] -= prod[q];
     });
+    if (!done && r < nj) publish(fcol + j * NJ + r);
   });
 }
 
