@@ -10,7 +10,14 @@ One step = the whole path on resident inputs: zero H, H += 2 X^T X over all
 tokens, damping + factorization -> U, the greedy column loop with lazy
 trailing updates, and packing.  Each stage is bracketed by HIP events on the
 stream the library launches on.  Prints one JSON line on stdout; progress
-goes to stderr.
+goes to stderr.  Besides the throughput the line holds: `roofline` (the
+Hessian accumulation, the dominant kernel, against the bf16 matrix peak),
+`e2e_roofline_frac` (the sum of every stage's time at its roofline divided
+by the measured step time, stage floors in `roofline_bound_ms`),
+`trailing_gemm` (the trailing update's kernels, timed by the profiler over
+one more quantize call, against the bf16 matrix peak) and `cpu_baseline`
+(the float64 oracle on a bounded sample of the same problem).  --layer small
+runs the 256 x 256 fp32 layer, whose oracle baseline is the whole problem.
 
 --workload gptq2d instead times two-sided rounding (gptq2d_round) of an n x n
 float64 matrix under seeded upper-triangular bases triu(I + 0.1 N(0,1)),
@@ -31,7 +38,49 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3    # MI355X fp32 matrix (and packed vector) peak
 PEAK_HBM_GBS = 8000.0
+
+
+def roofline_bound_ms(wl) -> dict:
+    """Time of each stage at its roofline (MI355X published peaks) and the sum
+    T_rl: SYRK n d(d+1) flop and trailing update d_out d_in (d_in - B) flop at
+    the bf16 matrix peak (the SYRK of fp32 X at the fp32 peak), factorization and triangular inverse 2 d^3 / 3 flop
+    and the column loop d_out d_in (B - 1) flop at the fp32 peak, packing (W
+    read, codes, fp16 scales and zeros written) at HBM bandwidth."""
+    d, n, do, b = wl.d_in, wl.n_tokens, wl.d_out, wl.block
+    ng = 1 if wl.group_size == -1 else d // wl.group_size
+    wbytes = 2 if wl.w_dtype == "bf16" else 4
+    t = {
+        "syrk": n * d * (d + 1) / ((PEAK_BF16_TFLOPS if wl.x_dtype == "bf16" else
+                                    PEAK_FP32_TFLOPS) * 1e9),
+        "factorization": (2.0 * d ** 3 / 3.0) / (PEAK_FP32_TFLOPS * 1e9),
+        "column_loop": do * d * (b - 1) / (PEAK_FP32_TFLOPS * 1e9),
+        "trailing": do * d * max(d - b, 0) / (PEAK_BF16_TFLOPS * 1e9),
+        "pack": (do * d * (wbytes + wl.bits / 8.0) + do * ng * 4) / (PEAK_HBM_GBS * 1e6),
+    }
+    t["total"] = sum(t.values())
+    return t
+
+
+def device_kernel_ms(fn, names):
+    """Device time (ms) of the kernels whose names contain any of `names`,
+    over one call of fn, from torch's profiler (which records every kernel the
+    process launches, the library's included); None if it records none."""
+    import torch
+    from torch.profiler import ProfilerActivity, profile
+    with profile(activities=[ProfilerActivity.CUDA]) as prof:
+        fn()
+        torch.cuda.synchronize()
+    tot, seen = 0.0, 0
+    for e in prof.events():
+        if str(getattr(e, "device_type", "")).endswith("CUDA") and any(k in e.name for k in names):
+            dt = getattr(e, "device_time", None)
+            if dt is None:
+                dt = getattr(e, "cuda_time", 0.0)
+            tot += float(dt)
+            seen += 1
+    return tot / 1e3 if seen else None
 
 
 def log(msg):
@@ -69,13 +118,13 @@ def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=Fal
     except Exception:  # pragma: no cover
         blas_threads = None
     cores = len(os.sched_getaffinity(0))
-    n_tok, n_rows = 4096, 256
+    n_tok, n_rows = min(4096, wl.n_tokens), min(256, wl.d_out)
     sub = synth.scaled(wl, n_tokens=n_tok, chunk_tokens=n_tok)
-    x = synth.as_f64(synth.x_chunk(sub, 0), "bf16")
+    x = synth.as_f64(synth.x_chunk(sub, 0), wl.x_dtype)
     t0 = time.perf_counter()
     H0 = oracle.hessian([x])
     t_h = (time.perf_counter() - t0) * (wl.n_tokens / n_tok)
-    W = synth.as_f64(synth.w_matrix(wl), "bf16")[:n_rows]
+    W = synth.as_f64(synth.w_matrix(wl), wl.w_dtype)[:n_rows]
     t_a = 0.0
     if act_order:
         t0 = time.perf_counter()
@@ -112,9 +161,10 @@ def cpu_baseline(wl, synth, max_seconds=30.0, act_order=False, static_groups=Fal
         "blas_threads": blas_threads,
         "kind": "oracle",
         "sample": (f"Hessian over {n_tok} of {wl.n_tokens} tokens (x{wl.n_tokens // n_tok}); "
-                   f"full 4096x4096 factorization; column loop and packing on {n_rows} of "
-                   f"{wl.d_out} rows (x{wl.d_out // n_rows}); float64 numpy/LAPACK, "
+                   f"full {wl.d_in}x{wl.d_in} factorization; column loop and packing on {n_rows} "
+                   f"of {wl.d_out} rows (x{wl.d_out // n_rows}); float64 numpy/LAPACK, "
                    f"elementwise numpy single-threaded"),
+        "seconds": total,
         "stage_seconds_extrapolated": {"hessian": t_h, "act_order": t_a, "prepare": t_p,
                                        "quantize": t_q, "pack": t_k},
     }
@@ -295,8 +345,8 @@ def bench_shared(args):
     status = torch.zeros(1, dtype=torch.int32, device=dev)
     rows = 2 * d_out
     ng = d_in // wl.group_size
-    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, gptq.GPTQ_BF16), dtype=torch.uint8,
-                       device=dev)
+    xcode = gptq.GPTQ_BF16 if wl.x_dtype == "bf16" else gptq.GPTQ_F32
+    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, xcode), dtype=torch.uint8, device=dev)
     ws_p = torch.empty(gptq.gptq_prepare_workspace(d_in), dtype=torch.uint8, device=dev)
     ws_q = torch.empty(gptq.gptq_quantize_workspace(rows, d_in, wl.block), dtype=torch.uint8,
                        device=dev)
@@ -388,10 +438,12 @@ def main():
     ap.add_argument("--workload", choices=["gptq", "gptq2d", "w4a16", "ffn_shared"],
                     default="gptq")
     ap.add_argument("--m", type=int, default=4096, help="rows of X for --workload w4a16")
-    ap.add_argument("--layer", choices=["attn7b", "l70b_sq", "l70b_up"], default="attn7b",
+    ap.add_argument("--layer", choices=["attn7b", "l70b_sq", "l70b_up", "small"],
+                    default="attn7b",
                     help="layer of the default workload: the 7B attention projection (4096 x "
-                         "4096, 262144 tokens), or the 70B-shaped 8192 x 8192 / 28672 x 8192 "
-                         "layers (65536 tokens)")
+                         "4096, 262144 tokens), the 70B-shaped 8192 x 8192 / 28672 x 8192 "
+                         "layers (65536 tokens), or the small fp32 layer (256 x 256, 2048 "
+                         "tokens with 4 outlier channels; the oracle runs it whole)")
     ap.add_argument("--n", type=int, default=1024, help="matrix size for --workload gptq2d")
     ap.add_argument("--act-order", action="store_true",
                     help="columns in activation order (gptq_act_order + the *_perm calls)")
@@ -416,17 +468,24 @@ def main():
     import torch
     from post_weight_quantization_syrk_amd import gptq, synth
 
-    wl = {"attn7b": synth.ATTN7B, "l70b_sq": synth.L70B_SQ, "l70b_up": synth.L70B_UP}[args.layer]
+    wl = {"attn7b": synth.ATTN7B, "l70b_sq": synth.L70B_SQ, "l70b_up": synth.L70B_UP,
+          "small": synth.SMALL}[args.layer]
     dev = "cuda:0"
     torch.cuda.set_device(0)
     gptq.lib()
     d_out, d_in, n = wl.d_out, wl.d_in, wl.n_tokens
-    log(f"generating inputs: X {n}x{d_in} bf16, W {d_out}x{d_in} bf16")
+    log(f"generating inputs: X {n}x{d_in} {wl.x_dtype}, W {d_out}x{d_in} {wl.w_dtype}")
     t0 = time.time()
+
+    def to_dev(a, dtype):
+        if dtype == "bf16":
+            return torch.from_numpy(a.view("int16")).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
     xb = synth.x_full(wl)
-    X = torch.from_numpy(xb.view("int16")).to(dev).view(torch.bfloat16)
+    X = to_dev(xb, wl.x_dtype)
     del xb
-    W = torch.from_numpy(synth.w_matrix(wl).view("int16")).to(dev).view(torch.bfloat16)
+    W = to_dev(synth.w_matrix(wl), wl.w_dtype)
     log(f"inputs resident in HBM ({time.time() - t0:.1f}s)")
 
     H = torch.zeros((d_in, d_in), dtype=torch.float32, device=dev)
@@ -440,8 +499,8 @@ def main():
     qweight = torch.empty((d_out, d_in * wl.bits // 32), dtype=torch.int32, device=dev)
     s16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
     z16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
-    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, gptq.GPTQ_BF16), dtype=torch.uint8,
-                       device=dev)
+    xcode = gptq.GPTQ_BF16 if wl.x_dtype == "bf16" else gptq.GPTQ_F32
+    ws_h = torch.empty(gptq.gptq_hessian_workspace(d_in, n, xcode), dtype=torch.uint8, device=dev)
     ws_p = torch.empty(gptq.gptq_prepare_workspace(d_in), dtype=torch.uint8, device=dev)
     ws_q = torch.empty(gptq.gptq_quantize_workspace(d_out, d_in, wl.block), dtype=torch.uint8,
                        device=dev)
@@ -510,18 +569,47 @@ def main():
     syrk_flops = float(n) * d_in * (d_in + 1)
     trail_flops = float(d_out) * d_in * (d_in - wl.block)
     syrk_tflops = syrk_flops / (stage_ms["hessian"] / 1e3) / 1e12
+    # bf16 X: matrix cores at the bf16 peak; fp32 X: the fp32 FMA kernel
+    # against the fp32 vector peak
+    syrk_peak = PEAK_BF16_TFLOPS if wl.x_dtype == "bf16" else PEAK_FP32_TFLOPS
+    syrk_kernel = "syrk_bf16_kernel" if wl.x_dtype == "bf16" else "syrk_f32_kernel"
     roofline = {
-        "kernel": "gptq_hessian_accumulate = syrk_bf16_kernel + splitk_reduce_kernel<256> (H += 2 X^T X)",
-        "bound": "mfma",
+        "kernel": (f"gptq_hessian_accumulate = {syrk_kernel} + splitk_reduce_kernel "
+                   f"(H += 2 X^T X)"),
+        "timing": ("HIP events on the library's stream around the whole call (both kernels), "
+                   "averaged over the timed steps"),
+        "bound": "mfma" if wl.x_dtype == "bf16" else "alu",
         "achieved": round(syrk_tflops, 2),
-        "peak": PEAK_BF16_TFLOPS,
+        "peak": syrk_peak,
         "unit": "TFLOP/s",
-        "frac": round(syrk_tflops / PEAK_BF16_TFLOPS, 4),
-        "traffic": traffic_from_profile(),
+        "frac": round(syrk_tflops / syrk_peak, 4),
+        "traffic": traffic_from_profile() if args.layer == "attn7b" else None,
         "algorithmic_flops_per_launch": syrk_flops,
         "avg_launch_ms": round(stage_ms["hessian"], 4),
     }
     upd_tflops = (syrk_flops + trail_flops) / ((stage_ms["hessian"] + stage_ms["quantize"]) / 1e3) / 1e12
+    rl = roofline_bound_ms(wl)
+    # the trailing update's own rate: its kernels (operand split + near and far
+    # updates) timed by the profiler over one more quantize call
+    trail_ms = None
+    if not order and d_in > wl.block:
+        try:
+            trail_ms = device_kernel_ms(
+                lambda: gptq.gptq_quantize_layer(W, U, dead, bits=wl.bits,
+                                                 group_size=wl.group_size, sym=wl.sym,
+                                                 block=wl.block, codes=codes, scales=scales,
+                                                 zeros=zeros, want_loss=False, ws=ws_q),
+                ("trailing3_kernel", "split_ut_kernel"))
+        except Exception as e:  # the profiler is optional here
+            log(f"trailing kernels not timed: {e}")
+    trailing = None
+    if trail_ms:
+        t_tf = trail_flops / (trail_ms / 1e3) / 1e12
+        trailing = {"kernels": "split_ut_kernel + trailing3_kernel<64> + trailing3_kernel<128>",
+                    "ms": round(trail_ms, 4), "algorithmic_flops": trail_flops,
+                    "achieved": round(t_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(t_tf / PEAK_BF16_TFLOPS, 4),
+                    "timing": "torch profiler device times over one quantize call"}
     line = {
         "metric": f"GPTQ weights quantized/sec/GPU ({d_out}x{d_in}, {n} tokens)",
         "value": round(value, 1),
@@ -533,11 +621,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": ("synthetic (seeded; stands in for a 7B model's weights and 128x2048 calibration "
-                 "tokens)" if args.layer == "attn7b" else
-                 "synthetic (seeded; stands in for a 70B model's layer weights and 65536 calibration "
-                 "tokens)"),
+        "dtype": wl.x_dtype,
+        "data": {"attn7b": "synthetic (seeded; stands in for a 7B model's weights and 128x2048 "
+                           "calibration tokens)",
+                 "small": "synthetic (seeded; fp32 layer with 4 outlier input channels x20)"}.get(
+                     args.layer, "synthetic (seeded; stands in for a 70B model's layer weights and "
+                                 "65536 calibration tokens)"),
         "config": {"workload": wl.name, "d_out": d_out, "d_in": d_in, "tokens": n,
                    "bits": wl.bits, "group_size": wl.group_size, "sym": wl.sym,
                    "block": wl.block, "damp": wl.damp, "act_order": bool(order),
@@ -548,6 +637,9 @@ def main():
                       "note": "(n d(d+1) + d_out d_in (d_in-128)) / (hessian + quantize stage "
                               "time); the quantize stage also holds the column loop"},
         "roofline": roofline,
+        "e2e_roofline_frac": round(rl["total"] / ms_step, 4),
+        "roofline_bound_ms": {k: round(v, 4) for k, v in rl.items()},
+        "trailing_gemm": trailing,
     }
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on a bounded sample (cpu_baseline)")
