@@ -33,6 +33,7 @@ constexpr int QB = 128;      // block width (columns)
 constexpr int UPITCH = 132;  // LDS pitch (floats) of the U block in the column loop
 constexpr int QG = 4;        // blocks per far trailing update
 constexpr int CL_LPR = 16;   // lanes per row in the column loop
+constexpr int64_t FAR_BIG_MIN = 2048;  // 128 x 128 far tiles from this many on
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -700,52 +701,57 @@ __global__ __launch_bounds__(256) void split_ut_kernel(const float* __restrict__
 // multiple of 64; rows past d_out and columns past n1 are loaded as clamped
 // copies of finite values, which only reach accumulator rows or columns that
 // are never stored.
-template <int TM>
-__global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
+template <int TM, int TN>
+__global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3_kernel(
+                                                        float* __restrict__ Wc,
                                                         const uint16_t* __restrict__ E3, int64_t se,
                                                         const uint16_t* __restrict__ Ut3,
                                                         int64_t su, int64_t d_out, int64_t d_in,
                                                         int64_t b0, int kb, int64_t n0,
                                                         int64_t n1) {
-  constexpr int TN = 64;
+  // each wave owns RB x CB of the tile's 32 x 32 blocks: the waves form a
+  // WR x WC grid over the tile's (TM / 32) x (TN / 32) blocks
   constexpr int NBLK = (TM / 32) * (TN / 32) / 4;  // 32 x 32 blocks per wave
-  constexpr int VP = TM * T3K / 8 / 256;           // 16-byte pieces per thread and part
-  static_assert(VP >= 1 && TN * T3K / 8 == 256, "one U^T piece per thread and part");
+  static_assert(NBLK == 1 || NBLK == 2 || NBLK == 4, "tile shape");
+  constexpr int RB = NBLK == 4 ? 2 : 1, CB = NBLK / RB;
+  constexpr int WC = (TN / 32) / CB;
+  static_assert(WC >= 1 && 4 % WC == 0 && (TM / 32) == (4 / WC) * RB, "wave grid");
+  constexpr int VP = TM * T3K / 8 / 256;  // 16-byte pieces per thread and part (delta)
+  constexpr int VQ = TN * T3K / 8 / 256;  // 16-byte pieces per thread and part (U^T)
+  static_assert(VP >= 1 && VQ >= 1, "whole pieces");
   __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], amid[TM * T3P], al[TM * T3P];
   __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bmid[TN * T3P], bl[TN * T3P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
+  const int wr = wave / WC, wc = wave % WC;
   const int64_t ncols = n1 - n0;
   const int ntn = (int)ceil_div(ncols, TN);
   const int64_t m0 = (int64_t)(blockIdx.x / ntn) * TM;
   const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * TN;
   const int rows = (int)min<int64_t>(TM, d_out - m0);
   const int cols = (int)min<int64_t>(TN, n1 - n0t);
-  // this wave's blocks: (bm, bn) with bm = row block, bn = column block
-  int bm[NBLK], bn[NBLK];
-#pragma unroll
-  for (int q = 0; q < NBLK; ++q) {
-    const int blk = wave * NBLK + q;  // row-block major over (TM / 32) x 2
-    bm[q] = blk >> 1;
-    bn[q] = blk & 1;
-  }
   float* C = Wc + m0 * d_in + n0t;
-  f32x16 acc[NBLK];
+  f32x16 acc[RB][CB];
 #pragma unroll
-  for (int q = 0; q < NBLK; ++q)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[q][i] = 0.0f;
-  // this thread's pieces: tile row r (clamped), k offset 8 (e % 4)
-  int64_t offp[VP];
+    for (int j = 0; j < CB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  // this thread's pieces: tile row (clamped), k offset 8 (e % 4)
+  int64_t offp[VP], offq[VQ];
 #pragma unroll
   for (int j = 0; j < VP; ++j) {
     const int e = j * 256 + tid, r = e >> 2;
     offp[j] = (m0 + (r < rows ? r : rows - 1)) * KC + 8 * (e & 3);
   }
-  const int nr = tid >> 2;
-  const int64_t offq = (n0t + (nr < cols ? nr : cols - 1)) * KC + 8 * (tid & 3);
+#pragma unroll
+  for (int j = 0; j < VQ; ++j) {
+    const int e = j * 256 + tid, r = e >> 2;
+    offq[j] = (n0t + (r < cols ? r : cols - 1)) * KC + 8 * (e & 3);
+  }
   // staged chunk, as 32-bit words (arrays of scalars stay in registers)
-  uint32_t xp[3 * VP * 4], xq[3 * 4];
+  uint32_t xp[3 * VP * 4], xq[3 * VQ * 4];
   auto gload = [&](int kc) __attribute__((always_inline)) {
     const int64_t ck = (b0 + kc) / KC;
     const uint16_t* pa = E3 + ck * 3 * se;
@@ -755,20 +761,24 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
 #pragma unroll
       for (int j = 0; j < VP; ++j) {
         const uint4 v = *(const uint4*)(pa + pt * se + offp[j]);
-        xp[4 * (3 * j + pt)] = v.x;
-        xp[4 * (3 * j + pt) + 1] = v.y;
-        xp[4 * (3 * j + pt) + 2] = v.z;
-        xp[4 * (3 * j + pt) + 3] = v.w;
+        const int x = 4 * (3 * j + pt);
+        xp[x] = v.x;
+        xp[x + 1] = v.y;
+        xp[x + 2] = v.z;
+        xp[x + 3] = v.w;
       }
-      const uint4 v = *(const uint4*)(pb + pt * su + offq);
-      xq[4 * pt] = v.x;
-      xq[4 * pt + 1] = v.y;
-      xq[4 * pt + 2] = v.z;
-      xq[4 * pt + 3] = v.w;
+#pragma unroll
+      for (int j = 0; j < VQ; ++j) {
+        const uint4 v = *(const uint4*)(pb + pt * su + offq[j]);
+        const int x = 4 * (3 * j + pt);
+        xq[x] = v.x;
+        xq[x + 1] = v.y;
+        xq[x + 2] = v.z;
+        xq[x + 3] = v.w;
+      }
     }
   };
-  auto lstore = [&](int kc) __attribute__((always_inline)) {
-    (void)kc;
+  auto lstore = [&]() __attribute__((always_inline)) {
     uint16_t* const pa[3] = {ah, amid, al};
     uint16_t* const pb[3] = {bh, bmid, bl};
 #pragma unroll
@@ -779,53 +789,73 @@ __global__ __launch_bounds__(256) void trailing3_kernel(float* __restrict__ Wc,
         const int x = 4 * (3 * j + pt);
         *(uint4*)(pa[pt] + r * T3P + c) = make_uint4(xp[x], xp[x + 1], xp[x + 2], xp[x + 3]);
       }
-      *(uint4*)(pb[pt] + nr * T3P + 8 * (tid & 3)) =
-          make_uint4(xq[4 * pt], xq[4 * pt + 1], xq[4 * pt + 2], xq[4 * pt + 3]);
+#pragma unroll
+      for (int j = 0; j < VQ; ++j) {
+        const int e = j * 256 + tid, r = e >> 2, c = 8 * (e & 3);
+        const int x = 4 * (3 * j + pt);
+        *(uint4*)(pb[pt] + r * T3P + c) = make_uint4(xq[x], xq[x + 1], xq[x + 2], xq[x + 3]);
+      }
     }
   };
   gload(0);
   for (int kc = 0; kc < kb; kc += T3K) {
     if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
-    lstore(kc);
+    lstore();
     __syncthreads();
     if (kc + T3K < kb) gload(kc + T3K);
 #pragma unroll
     for (int ks = 0; ks < T3K / 16; ++ks) {
       const int ko = 16 * ks + 8 * h;
+      bf16x8 a3[RB][3], b3[CB][3];
 #pragma unroll
-      for (int q = 0; q < NBLK; ++q) {
-        const int ar = (32 * bm[q] + l32) * T3P + ko, br = (32 * bn[q] + l32) * T3P + ko;
-        const bf16x8 a_h = *(const bf16x8*)(ah + ar), a_m = *(const bf16x8*)(amid + ar);
-        const bf16x8 a_l = *(const bf16x8*)(al + ar);
-        const bf16x8 b_h = *(const bf16x8*)(bh + br), b_m = *(const bf16x8*)(bmid + br);
-        const bf16x8 b_l = *(const bf16x8*)(bl + br);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_l, b_h, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_l, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_m, b_m, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_m, b_h, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_m, acc[q], 0, 0, 0);
-        acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_h, acc[q], 0, 0, 0);
+      for (int i = 0; i < RB; ++i) {
+        const int ar = (32 * (wr * RB + i) + l32) * T3P + ko;
+        a3[i][0] = *(const bf16x8*)(ah + ar);
+        a3[i][1] = *(const bf16x8*)(amid + ar);
+        a3[i][2] = *(const bf16x8*)(al + ar);
       }
+#pragma unroll
+      for (int j = 0; j < CB; ++j) {
+        const int br = (32 * (wc * CB + j) + l32) * T3P + ko;
+        b3[j][0] = *(const bf16x8*)(bh + br);
+        b3[j][1] = *(const bf16x8*)(bmid + br);
+        b3[j][2] = *(const bf16x8*)(bl + br);
+      }
+      // the six part products, smallest first: l h, h l, m m, m h, h m, h h
+#pragma unroll
+      for (int i = 0; i < RB; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) {
+          f32x16 c = acc[i][j];
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][2], b3[j][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][1], b3[j][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][1], b3[j][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][0], c, 0, 0, 0);
+          acc[i][j] = c;
+        }
     }
   }
-  // the tile's old values, all loads in flight together (clamped addresses),
-  // then Wc - acc
-  float old[NBLK][16];
+  // per block: its old values, the 16 loads in flight together (clamped
+  // addresses), then Wc - acc
 #pragma unroll
-  for (int q = 0; q < NBLK; ++q)
+  for (int i = 0; i < RB; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
-      const int c = 32 * bn[q] + l32;
-      old[q][i] = C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
-    }
+    for (int j = 0; j < CB; ++j) {
+      float old[16];
 #pragma unroll
-  for (int q = 0; q < NBLK; ++q)
+      for (int q = 0; q < 16; ++q) {
+        const int r = 32 * (wr * RB + i) + 8 * (q >> 2) + 4 * h + (q & 3);
+        const int c = 32 * (wc * CB + j) + l32;
+        old[q] = C[(int64_t)(r < rows ? r : rows - 1) * d_in + (c < cols ? c : cols - 1)];
+      }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int r = 32 * bm[q] + 8 * (i >> 2) + 4 * h + (i & 3);
-      const int c = 32 * bn[q] + l32;
-      if (r < rows && c < cols) C[(int64_t)r * d_in + c] = old[q][i] - acc[q][i];
+      for (int q = 0; q < 16; ++q) {
+        const int r = 32 * (wr * RB + i) + 8 * (q >> 2) + 4 * h + (q & 3);
+        const int c = 32 * (wc * CB + j) + l32;
+        if (r < rows && c < cols) C[(int64_t)r * d_in + c] = old[q] - acc[i][j][q];
+      }
     }
 }
 
@@ -969,17 +999,26 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        hipLaunchKernelGGL((trailing3_kernel<64>), dim3((unsigned)tiles), dim3(256), 0, stream,
+        hipLaunchKernelGGL((trailing3_kernel<64, 64>), dim3((unsigned)tiles), dim3(256), 0, stream,
                            w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
                            d_in, b0, QB, n0, gcol);
       }
     }
     if (gcol < d_in) {  // every block of the group is full
-      const int64_t tiles = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
+      // 128 x 128 tiles (half the LDS bytes per product, two waves per SIMD)
+      // when the launch still has enough of them to fill the chip several
+      // times over, else 128 x 64 (three waves per SIMD)
       const int kb = (int)(gcol - g0 * QB);
-      hipLaunchKernelGGL((trailing3_kernel<128>), dim3((unsigned)tiles), dim3(256), 0, stream,
-                         w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
-                         d_in, g0 * QB, kb, gcol, d_in);
+      const int64_t big = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 128);
+      if (big >= FAR_BIG_MIN)
+        hipLaunchKernelGGL((trailing3_kernel<128, 128>), dim3((unsigned)big), dim3(256), 0,
+                           stream, w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3,
+                           w.su, d_out, d_in, g0 * QB, kb, gcol, d_in);
+      else
+        hipLaunchKernelGGL((trailing3_kernel<128, 64>),
+                           dim3((unsigned)(ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64))),
+                           dim3(256), 0, stream, w.Wc, (const uint16_t*)w.E3, w.se,
+                           (const uint16_t*)w.Ut3, w.su, d_out, d_in, g0 * QB, kb, gcol, d_in);
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

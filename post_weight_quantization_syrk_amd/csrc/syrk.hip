@@ -12,8 +12,8 @@
 // the partials of each tile to H in split order, so results are deterministic
 // and no workgroup waits on another.
 //
-// fp32 inputs: a plain LDS-tiled fp32 FMA kernel (64 x 64 tiles) with the same
-// split-K / reduction structure.
+// fp32 inputs: 64 x 64 tiles on the fp32 matrix cores (v_mfma_f32_32x32x2f32)
+// with the same split-K / reduction structure.
 #include "common.h"
 #include "kernels.h"
 #include "mfma_f32.h"
@@ -568,7 +568,13 @@ __global__ __launch_bounds__(NTHR, 1) void syrk_bf16_kernel(SyrkArgs a) {
       }
 }
 
-// fp32 inputs: 64 x 64 tile per workgroup, 256 threads x (4 x 4) outputs.
+// fp32 inputs: 64 x 64 tile per workgroup on the fp32 matrix cores.  Each
+// wave owns a 32 x 32 quadrant and accumulates v_mfma_f32_32x32x2f32 over the
+// tokens two at a time: lane l supplies X[k0 + l / 32][column l % 32] of its
+// row and column quadrants, straight from the LDS stage.  The row pitch of 96
+// floats puts the two tokens' reads in opposite bank halves.
+constexpr int PF = TF + 32;
+
 struct SyrkF32Args {
   const float* X;
   int64_t ldx;
@@ -581,18 +587,21 @@ struct SyrkF32Args {
 };
 
 __global__ __launch_bounds__(256) void syrk_f32_kernel(SyrkF32Args a) {
-  __shared__ float sa[BKF][TF + 4];
-  __shared__ float sb[BKF][TF + 4];
+  __shared__ float sa[BKF][PF];
+  __shared__ float sb[BKF][PF];
   const int tile = blockIdx.x % a.ntri;  // split-major, as for bf16
   const int split = blockIdx.x / a.ntri;
   int ti, tj;
   tri_coords(tile, ti, tj);
   const int ci = ti * TF, cj = tj * TF;
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+  const int kl = lane >> 5, cl = lane & 31;
   const int64_t kb = (int64_t)split * a.kper;
   const int64_t ke = min(a.n, kb + a.kper);
-  float acc[4][4] = {};
+  f32x16 acc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
   for (int64_t k0 = kb; k0 < ke; k0 += BKF) {
     // 32 x 64 elements per operand, 8 per thread
     for (int e = tid; e < BKF * TF; e += 256) {
@@ -607,26 +616,21 @@ __global__ __launch_bounds__(256) void syrk_f32_kernel(SyrkF32Args a) {
       sb[kr][c] = vb;
     }
     __syncthreads();
-#pragma unroll 8
-    for (int k = 0; k < BKF; ++k) {
-      float av[4], bv[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        av[q] = sa[k][ty * 4 + q];
-        bv[q] = sb[k][tx * 4 + q];
-      }
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[p][q] = fmaf(av[p], bv[q], acc[p][q]);
+    for (int k = 0; k < BKF; k += 2) {
+      const float av = sa[k + kl][32 * wm + cl];
+      const float bv = sb[k + kl][32 * wn + cl];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
   float* out = a.partial + ((size_t)split * a.ntri + tile) * (size_t)(TF * TF);
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) out[(ty * 4 + p) * TF + tx * 4 + q] = acc[p][q];
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * wm + 8 * (r >> 2) + 4 * kl + (r & 3);
+    const int col = 32 * wn + cl;
+    out[row * TF + col] = acc[r];
+  }
 }
 
 

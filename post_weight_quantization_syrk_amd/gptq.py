@@ -107,10 +107,22 @@ def _check(status: int, where: str):
         raise GPTQError(status, where)
 
 
-def _workspace(nbytes: int, device) -> torch.Tensor | None:
+def _empty(stream, *args, **kw) -> torch.Tensor:
+    """torch.empty, allocated on the stream the call will launch on: the
+    caching allocator then hands the block out again only in that stream's
+    order, so a buffer dropped when the call returns (its scratch) cannot be
+    reused while the call's kernels still run on a stream other than the
+    current one."""
+    if stream is None:
+        return torch.empty(*args, **kw)
+    with torch.cuda.stream(stream):
+        return torch.empty(*args, **kw)
+
+
+def _workspace(nbytes: int, device, stream=None) -> torch.Tensor | None:
     if nbytes == 0:
         return None
-    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return _empty(stream, nbytes, dtype=torch.uint8, device=device)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -138,7 +150,7 @@ def gptq_hessian_accumulate(H: torch.Tensor, X: torch.Tensor, ws: torch.Tensor |
     n = X.shape[0]
     need = gptq_hessian_workspace(d, n, xd)
     if ws is None:
-        ws = _workspace(need, H.device)
+        ws = _workspace(need, H.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_hessian_accumulate(_ptr(H), d, _ptr(X), xd, n, X.stride(0), _ptr(ws),
                                          nbytes, _stream(stream)), "gptq_hessian_accumulate")
@@ -177,13 +189,13 @@ def gptq_prepare_hinv(H: torch.Tensor, damp: float = 0.01, U: torch.Tensor | Non
     d = H.shape[0]
     dev = H.device
     if U is None:
-        U = torch.empty((d, d), dtype=torch.float32, device=dev)
+        U = _empty(stream, (d, d), dtype=torch.float32, device=dev)
     if dead is None:
-        dead = torch.empty(d, dtype=torch.uint8, device=dev)
+        dead = _empty(stream, d, dtype=torch.uint8, device=dev)
     if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+        status = _empty(stream, 1, dtype=torch.int32, device=dev)
     if ws is None:
-        ws = _workspace(gptq_prepare_workspace(d), dev)
+        ws = _workspace(gptq_prepare_workspace(d), dev, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_prepare_hinv(_ptr(H), d, float(damp), _ptr(U), _ptr(dead), _ptr(status),
                                    _ptr(ws), nbytes, _stream(stream)), "gptq_prepare_hinv")
@@ -212,15 +224,15 @@ def gptq_quantize_layer(W: torch.Tensor, U: torch.Tensor, dead: torch.Tensor | N
         raise ValueError("W and U must be contiguous")
     ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
     if codes is None:
-        codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+        codes = _empty(stream, (d_out, d_in), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+        scales = _empty(stream, (d_out, max(ng, 1)), dtype=torch.float32, device=dev)
     if zeros is None:
-        zeros = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+        zeros = _empty(stream, (d_out, max(ng, 1)), dtype=torch.float32, device=dev)
     if loss_rows is None and want_loss:
-        loss_rows = torch.empty(d_out, dtype=torch.float32, device=dev)
+        loss_rows = _empty(stream, d_out, dtype=torch.float32, device=dev)
     if ws is None:
-        ws = _workspace(gptq_quantize_workspace(d_out, d_in, block), dev)
+        ws = _workspace(gptq_quantize_workspace(d_out, d_in, block), dev, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_quantize_layer(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U), _ptr(dead),
                                      bits, group_size, int(bool(sym)), block, _ptr(codes),
@@ -247,12 +259,12 @@ def gptq_quantize_layers(Ws: list, U: torch.Tensor, dead: torch.Tensor | None = 
     rows = [int(w.shape[0]) for w in Ws]
     total = sum(rows)
     ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
-    codes = torch.empty((total, d_in), dtype=torch.uint8, device=dev)
-    scales = torch.empty((total, max(ng, 1)), dtype=torch.float32, device=dev)
-    zeros = torch.empty((total, max(ng, 1)), dtype=torch.float32, device=dev)
-    loss_rows = torch.empty(total, dtype=torch.float32, device=dev) if want_loss else None
+    codes = _empty(stream, (total, d_in), dtype=torch.uint8, device=dev)
+    scales = _empty(stream, (total, max(ng, 1)), dtype=torch.float32, device=dev)
+    zeros = _empty(stream, (total, max(ng, 1)), dtype=torch.float32, device=dev)
+    loss_rows = _empty(stream, total, dtype=torch.float32, device=dev) if want_loss else None
     if ws is None:
-        ws = _workspace(gptq_quantize_workspace(total, d_in, block), dev)
+        ws = _workspace(gptq_quantize_workspace(total, d_in, block), dev, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     ptrs = (ctypes.c_void_p * len(Ws))(*[w.data_ptr() for w in Ws])
     dl = (ctypes.c_int64 * len(Ws))(*rows)
@@ -281,9 +293,9 @@ def gptq_act_order(X: torch.Tensor, d: int | None = None, perm=None, act_sum=Non
     d = X.shape[1] if d is None else d
     n = X.shape[0]
     if perm is None:
-        perm = torch.empty(d, dtype=torch.int32, device=X.device)
+        perm = _empty(stream, d, dtype=torch.int32, device=X.device)
     if ws is None:
-        ws = _workspace(gptq_act_order_workspace(d, n), X.device)
+        ws = _workspace(gptq_act_order_workspace(d, n), X.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_act_order(_ptr(X), _dtype_code(X), n, X.stride(0), d, _ptr(perm),
                                 _ptr(act_sum), _ptr(ws), nbytes, _stream(stream)),
@@ -300,13 +312,13 @@ def gptq_prepare_hinv_perm(H: torch.Tensor, perm: torch.Tensor | None, damp: flo
     if perm is not None and (perm.dtype != torch.int32 or perm.numel() != d):
         raise ValueError("perm must be an int32 tensor of d entries")
     if U is None:
-        U = torch.empty((d, d), dtype=torch.float32, device=dev)
+        U = _empty(stream, (d, d), dtype=torch.float32, device=dev)
     if dead is None:
-        dead = torch.empty(d, dtype=torch.uint8, device=dev)
+        dead = _empty(stream, d, dtype=torch.uint8, device=dev)
     if status is None:
-        status = torch.empty(1, dtype=torch.int32, device=dev)
+        status = _empty(stream, 1, dtype=torch.int32, device=dev)
     if ws is None:
-        ws = _workspace(gptq_prepare_workspace(d), dev)
+        ws = _workspace(gptq_prepare_workspace(d), dev, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_prepare_hinv_perm(_ptr(H), d, float(damp), _ptr(perm), _ptr(U), _ptr(dead),
                                         _ptr(status), _ptr(ws), nbytes, _stream(stream)),
@@ -335,17 +347,17 @@ def gptq_quantize_layer_perm(W: torch.Tensor, U: torch.Tensor, dead: torch.Tenso
         raise ValueError("perm must be an int32 tensor of d_in entries")
     ng = n_groups_for(d_in, group_size) if group_size > 0 or group_size == -1 else 1
     if codes is None:
-        codes = torch.empty((d_out, d_in), dtype=torch.uint8, device=dev)
+        codes = _empty(stream, (d_out, d_in), dtype=torch.uint8, device=dev)
     if scales is None:
-        scales = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+        scales = _empty(stream, (d_out, max(ng, 1)), dtype=torch.float32, device=dev)
     if zeros is None:
-        zeros = torch.empty((d_out, max(ng, 1)), dtype=torch.float32, device=dev)
+        zeros = _empty(stream, (d_out, max(ng, 1)), dtype=torch.float32, device=dev)
     if g_idx is None:
-        g_idx = torch.empty(d_in, dtype=torch.int32, device=dev)
+        g_idx = _empty(stream, d_in, dtype=torch.int32, device=dev)
     if loss_rows is None and want_loss:
-        loss_rows = torch.empty(d_out, dtype=torch.float32, device=dev)
+        loss_rows = _empty(stream, d_out, dtype=torch.float32, device=dev)
     if ws is None:
-        ws = _workspace(gptq_quantize_perm_workspace(d_out, d_in, block), dev)
+        ws = _workspace(gptq_quantize_perm_workspace(d_out, d_in, block), dev, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq_quantize_layer_perm(_ptr(W), _dtype_code(W), d_out, d_in, _ptr(U),
                                           _ptr(dead), _ptr(perm), int(bool(static_groups)), bits,
@@ -365,11 +377,11 @@ def gptq_pack(codes: torch.Tensor, scales: torch.Tensor, zeros: torch.Tensor | N
     words = (d_in * bits + 31) // 32
     ng = n_groups_for(d_in, group_size)
     if qweight is None:
-        qweight = torch.empty((d_out, words), dtype=torch.int32, device=dev)
+        qweight = _empty(stream, (d_out, words), dtype=torch.int32, device=dev)
     if scales_f16 is None:
-        scales_f16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+        scales_f16 = _empty(stream, (d_out, ng), dtype=torch.int16, device=dev)
     if zeros_f16 is None and not sym:
-        zeros_f16 = torch.empty((d_out, ng), dtype=torch.int16, device=dev)
+        zeros_f16 = _empty(stream, (d_out, ng), dtype=torch.int16, device=dev)
     _check(lib().gptq_pack(_ptr(codes), _ptr(scales), _ptr(zeros), d_out, d_in, bits, group_size,
                            int(bool(sym)), _ptr(qweight), _ptr(scales_f16), _ptr(zeros_f16),
                            _stream(stream)), "gptq_pack")
@@ -390,9 +402,9 @@ def gptq2d_round(Y: torch.Tensor, left_basis: torch.Tensor, right_basis: torch.T
         if t.shape != (n, n) or t.dtype != torch.float64 or not t.is_contiguous():
             raise ValueError(f"{name} must be a contiguous float64 [n, n] tensor")
     if Z is None:
-        Z = torch.empty((n, n), dtype=torch.float64, device=Y.device)
+        Z = _empty(stream, (n, n), dtype=torch.float64, device=Y.device)
     if ws is None:
-        ws = _workspace(gptq2d_workspace(n), Y.device)
+        ws = _workspace(gptq2d_workspace(n), Y.device, stream)
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().gptq2d_round(_ptr(Y), _ptr(left_basis), _ptr(right_basis), n, _ptr(Z), _ptr(ws),
                               nbytes, _stream(stream)), "gptq2d_round")
@@ -410,7 +422,7 @@ def gptq_w4a16_matmul(X: torch.Tensor, qweight: torch.Tensor, scales_f16: torch.
     m, d_in = X.shape
     d_out = qweight.shape[0]
     if Y is None:
-        Y = torch.empty((m, d_out), dtype=torch.float32, device=X.device)
+        Y = _empty(stream, (m, d_out), dtype=torch.float32, device=X.device)
     _check(lib().gptq_w4a16_matmul(_ptr(X), m, X.stride(0), _ptr(qweight), _ptr(scales_f16),
                                    _ptr(zeros_f16), d_out, d_in, group_size, int(bool(sym)),
                                    _ptr(Y), _stream(stream)), "gptq_w4a16_matmul")

@@ -379,3 +379,56 @@ def test_trailing_staging_paths_agree():
         b = _gpu_quant(dev_f32(W), U_off, dead, bits, g, sym)
         for key in ("codes", "scales", "zeros", "loss"):
             np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_side_stream_calls_match_current_stream():
+    """Every call launched on a stream other than the current one, with its
+    scratch allocated by the binding (on that stream), gives the same bits as
+    on the current stream; the side stream's work is not disturbed by
+    allocations made meanwhile on the current one."""
+    wl = synth.scaled(synth.ATTN7B, d_out=320, d_in=384, n_tokens=3000, chunk_tokens=3000)
+    xb = dev_bf16(synth.x_chunk(wl, 0))
+    W = dev_bf16(synth.w_matrix(wl))
+
+    def run(stream):
+        H = torch.zeros((wl.d_in, wl.d_in), dtype=torch.float32, device=DEV)
+        gptq.gptq_hessian_accumulate(H, xb, stream=stream)
+        U, dead, st = gptq.gptq_prepare_hinv(H, wl.damp, stream=stream)
+        out = gptq.gptq_quantize_layer(W, U, dead, bits=4, group_size=128, stream=stream)
+        # churn on the current stream while the side stream may still run
+        for _ in range(4):
+            torch.empty(8 << 20, dtype=torch.uint8, device=DEV).fill_(0xAB)
+        (torch.cuda.current_stream() if stream is None else stream).synchronize()
+        return [t.cpu() for t in (H, U) + tuple(out[:3])]
+
+    ref = run(None)
+    side = torch.cuda.Stream()
+    got = run(side)
+    for a, b in zip(ref, got):
+        assert torch.equal(a, b)
+
+
+def test_far_update_tile_shapes_agree_and_match_oracle():
+    """A layer tall enough for the 128 x 128 far-update tiles (65536 rows x 1024:
+    2048 of them) against the same first 4096 rows quantized alone (128 x 64
+    tiles): every element sums the same part products in the same k order, so
+    the two must agree bit for bit; and 32 sampled rows against the oracle."""
+    d_out, d_in = 65536, 1024
+    H32 = _spd(d_in, 21)
+    rng = np.random.default_rng(22)
+    W = (0.02 * rng.standard_normal((d_out, d_in))).astype(np.float32)
+    U, dead, _ = gptq.gptq_prepare_hinv(dev_f32(H32))
+    print("[far tiles] 65536 rows", flush=True)
+    tall = _gpu_quant(dev_f32(W), U, dead, 4, 128, False)
+    print("[far tiles] 4096 rows", flush=True)
+    part = _gpu_quant(dev_f32(W[:4096]), U, dead, 4, 128, False)
+    for k in ("codes", "scales", "zeros", "loss"):
+        np.testing.assert_array_equal(tall[k][:4096], part[k])
+    rows = np.sort(np.random.default_rng(23).choice(d_out, 32, replace=False))
+    p = oracle.prepare(H32.astype(np.float64))
+    ref = oracle.gptq(W[rows].astype(np.float64), p["U"], p["dead"], bits=4, group_size=128,
+                      sym=False, block=128)
+    sub = {k: v[rows] for k, v in tall.items()}
+    rep = compare_quant(sub, ref, group_size=128, bits=4, W=W[rows].astype(np.float64),
+                        H0=H32.astype(np.float64))
+    print(f"[far tiles] {rep}", flush=True)
