@@ -207,9 +207,12 @@ def bench_gptq2d(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_ev = e0.elapsed_time(e1) / args.steps
-    launches = 2 * n - 1
+    persistent = n <= 1024  # rows held in one wave's registers
+    launches = 1 if persistent else 2 * n - 1
+    hops = 2 * n - 1  # anti-diagonals: the dependent chain in either schedule
     gbs = gptq2d_bytes(n) / (ms_ev / 1e3) / 1e9
-    log(f"{ms:.3f} ms/step ({ms_ev:.3f} ms in events, {launches} anti-diagonal launches)")
+    log(f"{ms:.3f} ms/step ({ms_ev:.3f} ms in events, {launches} launches, "
+        f"{1e3 * ms_ev / hops:.2f} us per anti-diagonal)")
     line = {
         "metric": f"two-sided (GPTQ-2D) rounding, matrix entries/sec/GPU (n={n})",
         "value": round(n * n / (ms / 1e3), 1),
@@ -221,14 +224,18 @@ def bench_gptq2d(args):
         "data": "synthetic (seeded Y ~ N(0,1), bases triu(I + 0.1 N(0,1)))",
         "config": {"workload": f"gptq2d_two_sided_rounding_n{n}", "n": n},
         "roofline": {
-            "kernel": "g2d_diag_kernel (one launch per anti-diagonal)",
+            "kernel": ("g2d_rows_kernel (one persistent launch, a wave per row)" if persistent
+                       else "g2d_diag_kernel (one launch per anti-diagonal)"),
             "bound": "hbm",
             "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
             "algorithmic_bytes_per_launch": round(gptq2d_bytes(n) / launches, 1),
             "avg_launch_ms": round(ms_ev / launches, 5),
-            "note": "2n-1 dependent launches; the working set (3 n^2 float64) stays in "
-                    "the caches, so the per-launch latency, not HBM, sets the time",
+            "us_per_antidiagonal": round(1e3 * ms_ev / hops, 3),
+            "note": "a chain of 2n-1 dependent anti-diagonals; the working set (3 n^2 "
+                    "float64) stays in the caches, so the latency of each link (a "
+                    "value handed from one row's wave to the next, or a launch), not "
+                    "HBM, sets the time",
         },
     }
     if not args.no_cpu_baseline:

@@ -18,11 +18,28 @@
 // reads lies right of every column a lower entry writes, so the entries run
 // in parallel; kernel boundaries order the anti-diagonals.
 //
-// Layout: P row-major (the update of row i is a contiguous store); the read of
-// column j strides by n, but the entries of one anti-diagonal read adjacent
-// columns of the same rows, so neighbouring entries (the waves of a
-// workgroup) share cache lines.  R_R is transposed once (RT[j][c] = R_R[c][j])
-// so the update reads a contiguous row.  Everything is float64.
+// Two schedules, the same arithmetic per entry:
+//   n <= 1024, one persistent launch (g2d_rows_kernel).  Each wave owns one
+//     row i and walks it from j = n - 1 down to 0, holding row i of P (and of
+//     R_L) in registers.  P[k][j] receives its last term when row k handles
+//     entry (k, j), and entry (i, j) reads P[k][j] only for k > i, so it
+//     suffices that row i + 1 has finished column j (row i + 1 waited in turn
+//     for row i + 2, and so on).  After entry (i, j) the wave publishes the
+//     final P[i][j] into a write-once array F[j][i] (transposed: the reads of
+//     one entry are a contiguous run); F starts filled with a signalling NaN,
+//     which no float64 operation produces, so each value is its own "ready"
+//     flag.  F goes through memory with system-coherent accesses (the rows
+//     run on every XCD).  Every wait is bounded: a wait that gives up takes
+//     NaN for the value, which spreads to every entry that depends on it, so
+//     the launch always drains and Z shows the failure.  Rows go to waves in
+//     descending order, so a workgroup waits only on earlier workgroups.
+//   n > 1024, one launch per anti-diagonal (g2d_diag_kernel): P row-major in
+//     memory (the update of row i is a contiguous store); the read of column
+//     j strides by n, but the entries of one anti-diagonal read adjacent
+//     columns of the same rows, so neighbouring entries (the waves of a
+//     workgroup) share cache lines.
+// R_R is transposed once (RT[j][c] = R_R[c][j]) so the update reads a
+// contiguous row.  Everything is float64.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,16 +51,32 @@ namespace {
 
 constexpr int G2_WAVES = 4;  // entries per workgroup, one wave each
 
-// P = 0 and RT = R_R^T (upper triangle of R_R only; the rest of RT zero).
+// A signalling NaN: arithmetic only ever produces quiet NaNs, so no computed
+// value of P has these bits.
+constexpr uint64_t G2_EMPTY = 0x7FF4DEADBEEF0001ull;
+constexpr int G2_ROWS_MAX_NU = 16;  // register-resident rows: n <= 64 * 16
+
+__device__ __forceinline__ uint64_t sys_load(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+__device__ __forceinline__ void sys_store(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+}
+
+// RT = R_R^T (upper triangle of R_R only; the rest of RT zero) and the
+// running array: P = 0 (one launch per anti-diagonal) or F = empty (the
+// persistent launch, stored coherently like every later access to it).
 __global__ __launch_bounds__(256) void g2d_init_kernel(const double* __restrict__ RR,
                                                        double* __restrict__ RT,
-                                                       double* __restrict__ P, int n) {
+                                                       uint64_t* __restrict__ P, int n,
+                                                       int persistent) {
   const int64_t total = (int64_t)n * n;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
     const int j = (int)(e / n), c = (int)(e % n);
     RT[e] = (c <= j) ? RR[(int64_t)c * n + j] : 0.0;
-    P[e] = 0.0;
+    if (persistent) sys_store(P + e, G2_EMPTY);
+    else P[e] = 0;  // the bits of +0.0
   }
 }
 
@@ -122,7 +155,107 @@ __global__ __launch_bounds__(256) void g2d_diag_kernel(const double* __restrict_
   }
 }
 
+__device__ __forceinline__ double lane_value(double x, int src) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), src);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), src);
+  return __hiloint2double(hi, lo);
+}
+
+// Poll one entry of F until it holds a value or the wave's poll budget is
+// spent (then NaN, and the budget stays spent).
+__device__ __forceinline__ double wait_value(const uint64_t* p, int64_t& budget) {
+  uint64_t b = sys_load(p);
+  while (b == G2_EMPTY && budget > 0) {
+    __builtin_amdgcn_s_sleep(1);
+    b = sys_load(p);
+    --budget;
+  }
+  return b == G2_EMPTY ? __builtin_nan("") : __longlong_as_double((long long)b);
+}
+
+// The persistent schedule.  Wave w of the launch owns row i = n - 1 - w; lane
+// l holds columns c = l + 64 u, u < NU.  Entry (i, j):
+//   S = sum_{k >= i+2} R_L[i][k] F[j][k]   (rows two or more below: done with
+//                                          column j one step earlier)
+//     + R_L[i][i+1] F[j][i+1]              (waited for)
+//     + R_L[i][i] P[i][j]                  (own row, registers),
+// then Z, the published F[j][i] = P[i][j] + e R_R[j][j] (the same fused
+// multiply-add as the row update's), and the row update in registers.
+template <int NU>
+__global__ __launch_bounds__(256) void g2d_rows_kernel(const double* __restrict__ Y,
+                                                       const double* __restrict__ RL,
+                                                       const double* __restrict__ RT,
+                                                       uint64_t* __restrict__ F,
+                                                       double* __restrict__ Z, int n,
+                                                       int64_t spin) {
+  const int lane = threadIdx.x & 63;
+  const int i = n - 1 - ((int)blockIdx.x * G2_WAVES + (int)(threadIdx.x >> 6));
+  if (i < 0) return;
+  const double* rlrow = RL + (int64_t)i * n;
+  const int kb = i + 2;  // first row of the bulk sum
+  double rl[NU], p[NU];
+#pragma unroll
+  for (int u = 0; u < NU; ++u) {
+    const int c = lane + 64 * u;
+    rl[u] = (c >= kb && c < n) ? rlrow[c] : 0.0;
+    p[u] = 0.0;
+  }
+  const double rl_ii = rlrow[i];
+  const double rl_i1 = (i + 1 < n) ? rlrow[i + 1] : 0.0;
+  int64_t budget = spin;
+  for (int j = n - 1; j >= 0; --j) {
+    const uint64_t* frow = F + (int64_t)j * n;
+    const double* rtrow = RT + (int64_t)j * n;
+    double rt[NU];
+    uint64_t fb[NU];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int c = lane + 64 * u;
+      rt[u] = (c <= j) ? rtrow[c] : 0.0;
+      fb[u] = (c >= kb && c < n) ? sys_load(frow + c) : 0;  // 0: the bits of +0.0
+    }
+    const double y = Y[(int64_t)i * n + j];
+    const double rr = rtrow[j];
+    const double v = (i + 1 < n) ? wait_value(frow + i + 1, budget) : 0.0;
+    // the bulk was read before the wait: a value its row had not yet
+    // published is read again (rare), each lane drawing on its own copy of
+    // the wave's remaining budget; a lane that spends it ends the wave's
+    double acc0 = 0.0, acc1 = 0.0;
+    int64_t lb = budget;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      double f = __longlong_as_double((long long)fb[u]);
+      if (fb[u] == G2_EMPTY) f = wait_value(frow + lane + 64 * u, lb);
+      if (u & 1) acc1 = fma(rl[u], f, acc1);
+      else acc0 = fma(rl[u], f, acc0);
+    }
+    if (__any(lb <= 0)) budget = 0;
+    const double bulk = wave_sum(acc0 + acc1);
+    double pl = 0.0;
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      if (u == (j >> 6)) pl = p[u];
+    const double pj = lane_value(pl, j & 63);
+    const double S = fma(rl_ii, pj, fma(rl_i1, v, bulk));
+    const double z = rint(y + S / (rl_ii * rr));
+    const double e = y - z;
+    if (lane == 0) {
+      sys_store(F + (int64_t)j * n + i, (uint64_t)__double_as_longlong(fma(e, rr, pj)));
+      Z[(int64_t)i * n + j] = z;
+    }
+#pragma unroll
+    for (int u = 0; u < NU; ++u) p[u] = fma(e, rt[u], p[u]);
+  }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <int NU>
+void launch_rows(const double* Y, const double* RL, const double* RT, uint64_t* F, double* Z,
+                 int n, hipStream_t stream) {
+  hipLaunchKernelGGL(g2d_rows_kernel<NU>, dim3((unsigned)ceil_div(n, G2_WAVES)),
+                     dim3(64 * G2_WAVES), 0, stream, Y, RL, RT, F, Z, n, sync_spin_limit());
+}
 
 }  // namespace
 
@@ -137,7 +270,20 @@ hipError_t gptq2d_launch(const double* Y, const double* RL, const double* RR, in
   double* RT = (double*)((char*)ws + align256((size_t)n * n * sizeof(double)));
   const int64_t total = (int64_t)n * n;
   const int grid = (int)std::min<int64_t>(ceil_div(total, 256), 16384);
-  hipLaunchKernelGGL(g2d_init_kernel, dim3(grid), dim3(256), 0, stream, RR, RT, P, n);
+  const int nu = (int)ceil_div(n, 64);
+  const int persistent = nu <= G2_ROWS_MAX_NU;
+  hipLaunchKernelGGL(g2d_init_kernel, dim3(grid), dim3(256), 0, stream, RR, RT, (uint64_t*)P, n,
+                     persistent);
+  if (persistent) {
+    const double* RTc = RT;
+    uint64_t* F = (uint64_t*)P;
+    if (nu <= 1) launch_rows<1>(Y, RL, RTc, F, Z, n, stream);
+    else if (nu <= 2) launch_rows<2>(Y, RL, RTc, F, Z, n, stream);
+    else if (nu <= 4) launch_rows<4>(Y, RL, RTc, F, Z, n, stream);
+    else if (nu <= 8) launch_rows<8>(Y, RL, RTc, F, Z, n, stream);
+    else launch_rows<16>(Y, RL, RTc, F, Z, n, stream);
+    return hipGetLastError();
+  }
   for (int s = 2 * n - 2; s >= 0; --s) {
     const int m = std::min(s, n - 1) - std::max(0, s - n + 1) + 1;
     hipLaunchKernelGGL(g2d_diag_kernel, dim3((unsigned)ceil_div(m, G2_WAVES)),

@@ -78,6 +78,10 @@ hipError_t w4a16_launch(const void* X, int64_t m, int64_t ldx, const uint32_t* q
                         const uint16_t* scales_f16, const uint16_t* zeros_f16, int64_t d_out,
                         int64_t d_in, int group_size, float* Y, hipStream_t stream);
 
+// Polls a bounded wait between workgroups may take before it gives up
+// (environment GPTQ_SYNC_SPIN_LIMIT, default 2^20), read once per process.
+int64_t sync_spin_limit();
+
 // ---- two-sided rounding (anti-diagonal schedule) ----------------------------
 size_t gptq2d_workspace(int64_t n);
 hipError_t gptq2d_launch(const double* Y, const double* RL, const double* RR, int64_t n,

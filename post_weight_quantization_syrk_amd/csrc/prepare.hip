@@ -865,15 +865,15 @@ __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ 
 
 // Polls of a bounded wait before it gives up (GPTQ_SYNC_SPIN_LIMIT overrides;
 // a tiny value forces the timeout path, for tests of it).
-int64_t spin_limit() {
+}  // namespace
+
+int64_t sync_spin_limit() {
   static const int64_t v = [] {
     const char* e = std::getenv("GPTQ_SYNC_SPIN_LIMIT");
     return e ? std::max<int64_t>(0, std::atoll(e)) : ((int64_t)1 << 20);
   }();
   return v;
 }
-
-}  // namespace
 
 size_t prepare_workspace(int64_t d) {
   const size_t mat = align256((size_t)d * d * sizeof(float));
@@ -904,7 +904,7 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
                      stream, w.flags, nflags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int64_t spin = spin_limit();
+  const int64_t spin = sync_spin_limit();
   for (int c0 = 0; c0 < d; c0 += PW) {
     const int rows = (int)ceil_div(d - c0, NB);
     // passengers: the previous panel's update of the region from c0 + PW on

@@ -9,6 +9,10 @@ last bits and a value within that distance of a half-integer could round the
 other way.  With these seeded inputs none does, and Z must match exactly."""
 from __future__ import annotations
 
+import os
+import subprocess
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -38,7 +42,7 @@ def run_gpu(Y, RL, RR, **kw) -> np.ndarray:
     return Z.cpu().numpy()
 
 
-@pytest.mark.parametrize("n", [1, 2, 3, 16, 31, 32, 64, 65, 100, 256])
+@pytest.mark.parametrize("n", [1, 2, 3, 16, 31, 32, 64, 65, 100, 129, 256, 300, 513])
 def test_gptq2d_matches_oracle(n):
     print(f"[gptq2d] n={n}", flush=True)
     Y, RL, RR = synth.two_sided_inputs(n)
@@ -58,6 +62,51 @@ def test_gptq2d_largest_size():
     np.testing.assert_array_equal(Z, ref)
     # the feedback changes the result: plain rounding differs in many entries
     assert np.count_nonzero(Z != np.rint(Y)) > n
+
+
+def test_gptq2d_one_launch_per_antidiagonal_beyond_1024():
+    # rows of more than 1024 entries do not fit a wave's registers: this size
+    # takes the schedule with one launch per anti-diagonal
+    n = 1100
+    print(f"[gptq2d] n={n}", flush=True)
+    Y, RL, RR = synth.two_sided_inputs(n)
+    np.testing.assert_array_equal(run_gpu(Y, RL, RR), oracle.two_sided_antidiagonal(Y, RL, RR))
+
+
+_SPIN_CHILD = r"""
+import sys, numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+from post_weight_quantization_syrk_amd import gptq, synth
+n = int(sys.argv[2])
+Y, RL, RR = synth.two_sided_inputs(n)
+d = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+Z = gptq.gptq2d_round(d(Y), d(RL), d(RR))
+torch.cuda.synchronize()
+np.save(sys.argv[3], Z.cpu().numpy())
+"""
+
+
+def test_gptq2d_expired_waits_give_nan_and_drain(tmp_path):
+    """With no polls allowed (GPTQ_SYNC_SPIN_LIMIT=0, read once per process,
+    hence a child process), every wait that finds its value missing gives up
+    at once: the launch still completes, an entry whose inputs were all
+    present is exact, and every other entry is NaN.  The last row waits for
+    nothing."""
+    n = 300
+    print(f"[gptq2d] spin limit 0, n={n}", flush=True)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = str(tmp_path / "z.npy")
+    env = dict(os.environ, GPTQ_SYNC_SPIN_LIMIT="0")
+    r = subprocess.run([sys.executable, "-c", _SPIN_CHILD, root, str(n), out], env=env,
+                       timeout=300, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    Z = np.load(out)
+    Y, RL, RR = synth.two_sided_inputs(n)
+    ref = oracle.two_sided_antidiagonal(Y, RL, RR)
+    got = ~np.isnan(Z)
+    np.testing.assert_array_equal(Z[got], ref[got])
+    assert got[n - 1].all()
+    print(f"[gptq2d] entries present: {got.mean():.3f}", flush=True)
 
 
 def test_gptq2d_identity_bases_round_half_even():
