@@ -319,9 +319,10 @@ int gptq_w4a16_matmul(const void* X, int64_t m, int64_t ldx, const uint32_t* qwe
  *              copy of R_R.
  * n            1 .. GPTQ2D_MAX_N (0 is a no-op); larger n gives
  *              GPTQ_EUNSUPPORTED.  For n <= 1024 one persistent launch
- *              (a wave per row, rows handing values to each other through
- *              the workspace with bounded waits); beyond, 2n-1 dependent
- *              launches, one per anti-diagonal.  Both give the same Z.
+ *              (a wave per row; rows hand values to each other through
+ *              the workspace, and through LDS inside a workgroup, with
+ *              bounded waits); beyond, 2n-1 dependent launches, one per
+ *              anti-diagonal.  Both give the same Z.
  * A bounded wait that gives up (environment GPTQ_SYNC_SPIN_LIMIT polls,
  * default 2^20; not reached in a normal run) leaves NaN in every entry of Z
  * that depends on the missing value; the call still completes.
