@@ -701,6 +701,14 @@ __global__ __launch_bounds__(256) void split_ut_kernel(const float* __restrict__
 // multiple of 64; rows past d_out and columns past n1 are loaded as clamped
 // copies of finite values, which only reach accumulator rows or columns that
 // are never stored.
+//
+// Operand paths: each wave's error rows are its own (no other wave of the
+// workgroup reads them), so a lane loads its MFMA fragments of them straight
+// from memory into registers, 16 bytes per part and 16-k step, one chunk
+// ahead of the products; only the rows of U^T, which every wave of a column
+// of the wave grid reads, go through LDS.  Against staging both operands in
+// LDS this takes the error tile's LDS stores and reads off the LDS port,
+// which bound the kernel.
 template <int TM, int TN>
 __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3_kernel(
                                                         float* __restrict__ Wc,
@@ -716,18 +724,33 @@ __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3
   constexpr int RB = NBLK == 4 ? 2 : 1, CB = NBLK / RB;
   constexpr int WC = (TN / 32) / CB;
   static_assert(WC >= 1 && 4 % WC == 0 && (TM / 32) == (4 / WC) * RB, "wave grid");
-  constexpr int VP = TM * T3K / 8 / 256;  // 16-byte pieces per thread and part (delta)
   constexpr int VQ = TN * T3K / 8 / 256;  // 16-byte pieces per thread and part (U^T)
-  static_assert(VP >= 1 && VQ >= 1, "whole pieces");
-  __shared__ __attribute__((aligned(16))) uint16_t ah[TM * T3P], amid[TM * T3P], al[TM * T3P];
+  static_assert(VQ >= 1, "whole pieces");
+  constexpr int KS = T3K / 16;            // 16-k MFMA steps per chunk
   __shared__ __attribute__((aligned(16))) uint16_t bh[TN * T3P], bmid[TN * T3P], bl[TN * T3P];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int h = lane >> 5, l32 = lane & 31;
   const int wr = wave / WC, wc = wave % WC;
   const int64_t ncols = n1 - n0;
   const int ntn = (int)ceil_div(ncols, TN);
-  const int64_t m0 = (int64_t)(blockIdx.x / ntn) * TM;
-  const int64_t n0t = n0 + (int64_t)(blockIdx.x % ntn) * TN;
+  const int ntm = (int)ceil_div(d_out, TM);
+  // XCD-aware tile order.  Workgroup ids go to the eight XCDs round-robin,
+  // and each XCD's L2 is its own, so id t = 8 i + x takes rank x T8 + i (T8 =
+  // ranks per XCD) of an order in which consecutive ranks are close: row
+  // bands of a quarter of the row tiles, and inside a band column after
+  // column.  Each XCD then holds a quarter of the rows by half of the
+  // columns, and fetches a quarter of the errors and half of U^T instead of
+  // all the errors.  The grid is rounded up to a multiple of eight; the
+  // padding ranks exit.
+  const int ntiles = ntm * ntn;
+  const int t8 = (int)ceil_div(ntiles, 8);
+  const int rank = ((int)blockIdx.x % 8) * t8 + (int)blockIdx.x / 8;
+  if (rank >= ntiles) return;
+  const int hb = (int)ceil_div(ntm, 4);
+  const int band = rank / (hb * ntn), within = rank % (hb * ntn);
+  const int bh_rows = min(hb, ntm - band * hb);
+  const int64_t m0 = (int64_t)(band * hb + within % bh_rows) * TM;
+  const int64_t n0t = n0 + (int64_t)(within / bh_rows) * TN;
   const int rows = (int)min<int64_t>(TM, d_out - m0);
   const int cols = (int)min<int64_t>(TN, n1 - n0t);
   float* C = Wc + m0 * d_in + n0t;
@@ -738,35 +761,26 @@ __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3
     for (int j = 0; j < CB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-  // this thread's pieces: tile row (clamped), k offset 8 (e % 4)
-  int64_t offp[VP], offq[VQ];
+  // this lane's error rows (clamped) and k offset inside a 16-k step
+  int64_t offa[RB];
 #pragma unroll
-  for (int j = 0; j < VP; ++j) {
-    const int e = j * 256 + tid, r = e >> 2;
-    offp[j] = (m0 + (r < rows ? r : rows - 1)) * KC + 8 * (e & 3);
+  for (int i = 0; i < RB; ++i) {
+    const int r = 32 * (wr * RB + i) + l32;
+    offa[i] = (m0 + (r < rows ? r : rows - 1)) * KC + 8 * h;
   }
+  // this thread's pieces of the U^T tile: tile row (clamped), k offset 8 (e % 4)
+  int64_t offq[VQ];
 #pragma unroll
   for (int j = 0; j < VQ; ++j) {
     const int e = j * 256 + tid, r = e >> 2;
     offq[j] = (n0t + (r < cols ? r : cols - 1)) * KC + 8 * (e & 3);
   }
-  // staged chunk, as 32-bit words (arrays of scalars stay in registers)
-  uint32_t xp[3 * VP * 4], xq[3 * VQ * 4];
+  // staged U^T chunk, as 32-bit words (arrays of scalars stay in registers)
+  uint32_t xq[3 * VQ * 4];
   auto gload = [&](int kc) __attribute__((always_inline)) {
-    const int64_t ck = (b0 + kc) / KC;
-    const uint16_t* pa = E3 + ck * 3 * se;
-    const uint16_t* pb = Ut3 + ck * 3 * su;
+    const uint16_t* pb = Ut3 + ((b0 + kc) / KC) * 3 * su;
 #pragma unroll
-    for (int pt = 0; pt < 3; ++pt) {
-#pragma unroll
-      for (int j = 0; j < VP; ++j) {
-        const uint4 v = *(const uint4*)(pa + pt * se + offp[j]);
-        const int x = 4 * (3 * j + pt);
-        xp[x] = v.x;
-        xp[x + 1] = v.y;
-        xp[x + 2] = v.z;
-        xp[x + 3] = v.w;
-      }
+    for (int pt = 0; pt < 3; ++pt)
 #pragma unroll
       for (int j = 0; j < VQ; ++j) {
         const uint4 v = *(const uint4*)(pb + pt * su + offq[j]);
@@ -776,44 +790,35 @@ __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3
         xq[x + 2] = v.z;
         xq[x + 3] = v.w;
       }
-    }
   };
   auto lstore = [&]() __attribute__((always_inline)) {
-    uint16_t* const pa[3] = {ah, amid, al};
     uint16_t* const pb[3] = {bh, bmid, bl};
 #pragma unroll
-    for (int pt = 0; pt < 3; ++pt) {
-#pragma unroll
-      for (int j = 0; j < VP; ++j) {
-        const int e = j * 256 + tid, r = e >> 2, c = 8 * (e & 3);
-        const int x = 4 * (3 * j + pt);
-        *(uint4*)(pa[pt] + r * T3P + c) = make_uint4(xp[x], xp[x + 1], xp[x + 2], xp[x + 3]);
-      }
+    for (int pt = 0; pt < 3; ++pt)
 #pragma unroll
       for (int j = 0; j < VQ; ++j) {
         const int e = j * 256 + tid, r = e >> 2, c = 8 * (e & 3);
         const int x = 4 * (3 * j + pt);
         *(uint4*)(pb[pt] + r * T3P + c) = make_uint4(xq[x], xq[x + 1], xq[x + 2], xq[x + 3]);
       }
-    }
   };
-  gload(0);
-  for (int kc = 0; kc < kb; kc += T3K) {
-    if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
-    lstore();
-    __syncthreads();
-    if (kc + T3K < kb) gload(kc + T3K);
+  // the error fragments of one chunk: [row block][16-k step][part]
+  typedef uint4 AFrag[RB][KS][3];
+  auto aload = [&](AFrag& a, int kc) __attribute__((always_inline)) {
+    const uint16_t* pa = E3 + ((b0 + kc) / KC) * 3 * se;
 #pragma unroll
-    for (int ks = 0; ks < T3K / 16; ++ks) {
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt)
+          a[i][ks][pt] = *(const uint4*)(pa + pt * se + offa[i] + 16 * ks);
+  };
+  auto products = [&](const AFrag& a) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
       const int ko = 16 * ks + 8 * h;
-      bf16x8 a3[RB][3], b3[CB][3];
-#pragma unroll
-      for (int i = 0; i < RB; ++i) {
-        const int ar = (32 * (wr * RB + i) + l32) * T3P + ko;
-        a3[i][0] = *(const bf16x8*)(ah + ar);
-        a3[i][1] = *(const bf16x8*)(amid + ar);
-        a3[i][2] = *(const bf16x8*)(al + ar);
-      }
+      bf16x8 b3[CB][3];
 #pragma unroll
       for (int j = 0; j < CB; ++j) {
         const int br = (32 * (wc * CB + j) + l32) * T3P + ko;
@@ -823,19 +828,53 @@ __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3
       }
       // the six part products, smallest first: l h, h l, m m, m h, h m, h h
 #pragma unroll
-      for (int i = 0; i < RB; ++i)
+      for (int i = 0; i < RB; ++i) {
+        const bf16x8 ah = __builtin_bit_cast(bf16x8, a[i][ks][0]);
+        const bf16x8 am = __builtin_bit_cast(bf16x8, a[i][ks][1]);
+        const bf16x8 al = __builtin_bit_cast(bf16x8, a[i][ks][2]);
 #pragma unroll
         for (int j = 0; j < CB; ++j) {
           f32x16 c = acc[i][j];
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][2], b3[j][0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][2], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][1], b3[j][1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][1], b3[j][0], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][1], c, 0, 0, 0);
-          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a3[i][0], b3[j][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, b3[j][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b3[j][2], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, b3[j][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, b3[j][0], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b3[j][1], c, 0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, b3[j][0], c, 0, 0, 0);
           acc[i][j] = c;
         }
+      }
     }
+  };
+  // one chunk: publish its U^T rows in LDS, start the loads of chunk kn,
+  // multiply with this chunk's error fragments (a); chunk kn's go to an.
+  // The loads are unconditional (the last chunk loads itself again), so
+  // every path has the same loads in flight and the wait before the
+  // products only covers the fragments they use; a branch around them made
+  // the compiler wait for every load there.
+  auto chunk = [&](const AFrag& a, AFrag& an, int kc, int kn) __attribute__((always_inline)) {
+    if (kc > 0) __syncthreads();  // the previous chunk's products are done with LDS
+    lstore();
+    __syncthreads();
+    gload(kn);
+    __builtin_amdgcn_sched_barrier(0);
+    aload(an, kn);
+    // keep the loads ahead of the products and in the same order on every
+    // path (the scheduler would otherwise sink them next to their first use,
+    // a chunk later in program order but not in time)
+    __builtin_amdgcn_sched_barrier(0);
+    products(a);
+  };
+  // the launches give kb a multiple of 4 chunks (whole 128-column blocks)
+  AFrag a0, a1;
+  gload(0);
+  __builtin_amdgcn_sched_barrier(0);
+  aload(a0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int klast = kb - T3K;
+  for (int kc = 0; kc < kb; kc += 2 * T3K) {
+    chunk(a0, a1, kc, min(kc + T3K, klast));
+    chunk(a1, a0, kc + T3K, min(kc + 2 * T3K, klast));
   }
   // per block: its old values, the 16 loads in flight together (clamped
   // addresses), then Wc - acc
@@ -999,7 +1038,8 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
       const int64_t n0 = b0 + QB;
       if (b + 1 < gend) {  // blocks before the group's last are full
         const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        hipLaunchKernelGGL((trailing3_kernel<64, 64>), dim3((unsigned)tiles), dim3(256), 0, stream,
+        hipLaunchKernelGGL((trailing3_kernel<64, 64>), dim3((unsigned)(8 * ceil_div(tiles, 8))),
+                           dim3(256), 0, stream,
                            w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
                            d_in, b0, QB, n0, gcol);
       }
@@ -1010,13 +1050,13 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
       // times over, else 128 x 64 (three waves per SIMD)
       const int kb = (int)(gcol - g0 * QB);
       const int64_t big = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 128);
+      const int64_t small = ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64);
       if (big >= FAR_BIG_MIN)
-        hipLaunchKernelGGL((trailing3_kernel<128, 128>), dim3((unsigned)big), dim3(256), 0,
-                           stream, w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3,
-                           w.su, d_out, d_in, g0 * QB, kb, gcol, d_in);
+        hipLaunchKernelGGL((trailing3_kernel<128, 128>), dim3((unsigned)(8 * ceil_div(big, 8))),
+                           dim3(256), 0, stream, w.Wc, (const uint16_t*)w.E3, w.se,
+                           (const uint16_t*)w.Ut3, w.su, d_out, d_in, g0 * QB, kb, gcol, d_in);
       else
-        hipLaunchKernelGGL((trailing3_kernel<128, 64>),
-                           dim3((unsigned)(ceil_div(d_out, 128) * ceil_div(d_in - gcol, 64))),
+        hipLaunchKernelGGL((trailing3_kernel<128, 64>), dim3((unsigned)(8 * ceil_div(small, 8))),
                            dim3(256), 0, stream, w.Wc, (const uint16_t*)w.E3, w.se,
                            (const uint16_t*)w.Ut3, w.su, d_out, d_in, g0 * QB, kb, gcol, d_in);
     }
