@@ -820,7 +820,17 @@ __global__ __launch_bounds__(256) void inv_level_kernel(const float* __restrict_
   if (*status != 0) return;
   __shared__ __attribute__((aligned(16))) float lds[Tile::lds_floats];
   const int sb = s / NB;  // tiles per half
-  const int t = blockIdx.x;
+  // Rank of this workgroup in the longest-first order.  When the whole grid
+  // is resident at once (up to four workgroups per CU), nothing is handed
+  // out as CUs free up, so longest-first would give the first CUs all the
+  // long tiles: workgroups t, t + 256, t + 512, t + 768 share a CU, and a
+  // snake over blocks of 256 ranks (odd blocks reversed) gives every CU a
+  // mix of long and short tiles with about the same total.
+  int t = blockIdx.x;
+  if (gridDim.x <= 4 * 256) {
+    const int blk = t >> 8, r = t & 255;
+    t = (blk & 1) ? (blk << 8) + min(255, (int)gridDim.x - 1 - (blk << 8)) - r : t;
+  }
   const int major = t / (pairs * sb), rem = t % (pairs * sb);
   const int p = rem / sb, minor = rem % sb;
   const int rt = XSTEP ? sb - 1 - major : minor, ct = XSTEP ? minor : major;
