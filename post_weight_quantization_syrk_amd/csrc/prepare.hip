@@ -33,6 +33,7 @@
 
 #include <algorithm>
 #include <cstdlib>
+#include <vector>
 
 namespace gptq {
 
@@ -619,20 +620,111 @@ __device__ __forceinline__ void syrk_tile(float* __restrict__ A, int d, int c0, 
 
 constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 
+// ---- the inverse L^{-1} by recursive doubling --------------------------
+// Level s (a power of two times 64): pairs (a, b = a + s, e = min(b + s, d)),
+// a = 0, 2s, 4s, ..., b < d, with
+//   inv([L11 0; L21 L22]) = [X11 0; -X22 L21 X11  X22]
+// in two steps over 64 x 64 tiles (sb = s / 64, sb^2 tiles per pair):
+//   T step: T[b:e, a:b] = L[b:e, a:b] M[a:b, a:b]   (M lower: k >= 64 ct)
+//   X step: M[b:e, a:b] = -M[b:e, b:e] T[b:e, a:b]  (M lower: k < 64 rt + 64)
+// starting from the diagonal blocks' inverses, which the factorization writes
+// into M.  A step's tiles are numbered g = pair * sb^2 + local, the local
+// order longest tile first (ct ascending for T, rt descending for X).  A T
+// tile needs L's columns a .. b final and M[a:b, a:b] complete; an X tile
+// needs its pair's T tiles and M[b:e, b:e].  The host hands each launch the
+// tiles whose operands are complete when it starts: the factorization's
+// launches carry the ones that are ready before it ends (on the CUs its
+// latency-bound chain leaves idle), inv_items_kernel the rest.  The T regions
+// (and the X regions of M) of different pairs and levels are disjoint, and
+// every tile does the same arithmetic whichever launch runs it.
+constexpr int INV_ITEMS = 16;
+struct InvItems {  // tiles g0[i] .. g0[i] + cnt[i] - 1 of step (s[i], x[i]), in order
+  int n;
+  int s[INV_ITEMS], x[INV_ITEMS], g0[INV_ITEMS], cnt[INV_ITEMS];
+};
+using InvTile = MfmaTile<NB, NB, 32, false>;  // C = P Q with Q row-major
+
+template <bool XSTEP>
+__device__ __forceinline__ void inv_tile(const float* __restrict__ L, float* __restrict__ M,
+                                         float* __restrict__ Tb, int d, int s, int g, float* lds) {
+  using Tile = InvTile;
+  const int sb = s / NB;
+  const int p = g / (sb * sb), lt = g % (sb * sb);
+  const int major = lt / sb, minor = lt % sb;
+  const int rt = XSTEP ? sb - 1 - major : minor, ct = XSTEP ? minor : major;
+  const int a = 2 * s * p, b = a + s;
+  const int i0 = b + NB * rt, j0 = a + NB * ct;
+  if (i0 >= d) return;
+  const int ib = min(NB, d - i0);
+  const int k_lo = XSTEP ? 0 : NB * ct, k_hi = XSTEP ? min(NB * rt + NB, d - b) : s;
+  const float* Pb = XSTEP ? M + (int64_t)i0 * d + b : L + (int64_t)i0 * d + a;
+  const float* Qb = XSTEP ? Tb + (int64_t)b * d + j0 : M + (int64_t)a * d + j0;
+  f32x16 acc[Tile::FM][Tile::FN];
+  Tile::zero(acc);
+  typename Tile::PQRegs v;
+  auto fetch = [&](int k) __attribute__((always_inline)) {
+    const int kn = min(32, k_hi - k);
+    Tile::fetch_pq(v, Pb + k, d, ib, kn, Qb + (int64_t)k * d, d, kn, NB);
+  };
+  fetch(k_lo);
+  for (int k = k_lo; k < k_hi; k += 32) {
+    const int kn = min(32, k_hi - k);
+    if (k > k_lo) __syncthreads();
+    Tile::template stage_pq<XSTEP>(lds, v, ib, kn, kn, NB);
+    __syncthreads();
+    if (k + 32 < k_hi) fetch(k + 32);
+    Tile::mma(lds, acc);
+  }
+  float* C = (XSTEP ? M : Tb) + (int64_t)i0 * d + j0;
+  Tile::template store<false>(C, d, ib, NB, acc);
+}
+
+// Tile k of a launch's items (k < the sum of cnt).
+__device__ __forceinline__ void inv_item_tile(const InvItems& it, int k, const float* L, float* M,
+                                              float* Tb, int d, float* lds) {
+  int s = 0, x = 0, g = -1;
+#pragma unroll
+  for (int i = 0; i < INV_ITEMS; ++i) {
+    if (g < 0 && i < it.n) {
+      if (k < it.cnt[i]) {
+        s = it.s[i];
+        x = it.x[i];
+        g = it.g0[i] + k;
+      } else {
+        k -= it.cnt[i];
+      }
+    }
+  }
+  if (g < 0) return;
+  if (x)
+    inv_tile<true>(L, M, Tb, d, s, g, lds);
+  else
+    inv_tile<false>(L, M, Tb, d, s, g, lds);
+}
+
 // Workgroups past the panel's row blocks (blockIdx.x >= rows) are passengers:
-// they apply the previous panel [pc0, c0) to the trailing tiles from c0 + PW on
-// (128 x 128 lower tiles of that region), which this panel does not touch.
+// the first `rest` apply the previous panel [pc0, c0) to the trailing tiles
+// from c0 + PW on (128 x 128 lower tiles of that region), which this panel does
+// not touch; the others are tiles of the inverse whose operands were complete
+// when the launch started (inv_tile: they read L's columns before c0 and M, T,
+// which nothing else in the launch writes).
 __global__ __launch_bounds__(256) void chol_panel_kernel(float* __restrict__ A,
                                                          float* __restrict__ M,
                                                          float* __restrict__ Dinv,
                                                          int* __restrict__ flags, int d, int c0,
-                                                         int rows, int pc0,
+                                                         int rows, int pc0, int rest,
+                                                         float* __restrict__ Tb, InvItems inv,
                                                          int32_t* status, int64_t spin) {
   if (*status != 0) return;
   constexpr size_t LDS_FLOATS =
-      cmax(cmax(TileT::lds_floats, DIAG_LDS_FLOATS), MfmaTile<128, 128, 32, true>::lds_floats);
+      cmax(cmax(cmax(TileT::lds_floats, DIAG_LDS_FLOATS), MfmaTile<128, 128, 32, true>::lds_floats),
+           InvTile::lds_floats);
   __shared__ __attribute__((aligned(16))) float lds[LDS_FLOATS];
   __shared__ int ok_lds;
+  if ((int)blockIdx.x >= rows + rest) {
+    inv_item_tile(inv, (int)blockIdx.x - rows - rest, A, M, Tb, d, lds);
+    return;
+  }
   if ((int)blockIdx.x >= rows) {
     int ti, tj;
     tri_coords((int)blockIdx.x - rows, ti, tj);
@@ -793,72 +885,45 @@ __device__ __forceinline__ void syrk_tile(float* __restrict__ A, int d, int c0, 
 }
 
 // The band after panel [c0, c1): tiles (rows c1 + 64 i, columns c1 + 64 j) of
-// the next panel's columns, lower ones only.
+// the next panel's columns, lower ones only; workgroups past the band's
+// ntiles are short tiles of the inverse (inv_tile) that were ready when the
+// launch started.
 __global__ __launch_bounds__(256) void chol_band_kernel(float* __restrict__ A, int d, int c0,
-                                                        int c1, int nbc, const int32_t* status) {
+                                                        int c1, int nbc, int ntiles,
+                                                        float* __restrict__ M,
+                                                        float* __restrict__ Tb, InvItems inv,
+                                                        const int32_t* status) {
   if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[MfmaTile<64, 64, 32, true>::lds_floats];
+  __shared__ __attribute__((aligned(16))) float
+      lds[cmax(MfmaTile<64, 64, 32, true>::lds_floats, InvTile::lds_floats)];
+  if ((int)blockIdx.x >= ntiles) {
+    inv_item_tile(inv, (int)blockIdx.x - ntiles, A, M, Tb, d, lds);
+    return;
+  }
   const int i = blockIdx.x / nbc, j = blockIdx.x % nbc;
   if (j > i) return;
   syrk_tile<64>(A, d, c0, c1, c1 + 64 * i, c1 + 64 * j, lds);
 }
 
-// ---- the inverse: recursive doubling ------------------------------------
-// Level s (a power of two times 64): pairs (a, b = a + s, e = min(b + s, d)),
-// a = 0, 2s, 4s, ..., b < d.  Tile (rt, ct) of a pair covers rows b + 64 rt ..
-// and columns a + 64 ct ..; (s / 64)^2 tiles per pair.
-//   T step: T[b:e, a:b] = L[b:e, a:b] M[a:b, a:b]   (M lower: k >= 64 ct)
-//   X step: M[b:e, a:b] = -M[b:e, b:e] T[b:e, a:b]  (M lower: k < 64 rt + 64)
-// A tile's work grows with its K range (the triangle), so workgroups are
-// numbered longest tile first (ct ascending for T, rt descending for X).
-template <bool XSTEP>
-__global__ __launch_bounds__(256) void inv_level_kernel(const float* __restrict__ L,
+// The inverse's tiles that were not carried by the factorization's launches:
+// one launch per round of tiles whose operands are complete (inv_tile).
+// When the whole grid is resident at once (up to four workgroups per CU),
+// nothing is handed out as CUs free up, so the longest-first order would give
+// the first CUs all the long tiles: workgroups t, t + 256, t + 512, t + 768
+// share a CU, and a snake over blocks of 256 (odd blocks reversed) gives every
+// CU a mix of long and short tiles with about the same total.
+__global__ __launch_bounds__(256) void inv_items_kernel(const float* __restrict__ L,
                                                         float* __restrict__ M,
-                                                        float* __restrict__ Tb, int d, int s,
-                                                        int pairs, const int32_t* status) {
-  using Tile = MfmaTile<NB, NB, 32, false>;  // C = P Q with Q row-major
+                                                        float* __restrict__ Tb, int d,
+                                                        InvItems items, const int32_t* status) {
   if (*status != 0) return;
-  __shared__ __attribute__((aligned(16))) float lds[Tile::lds_floats];
-  const int sb = s / NB;  // tiles per half
-  // Rank of this workgroup in the longest-first order.  When the whole grid
-  // is resident at once (up to four workgroups per CU), nothing is handed
-  // out as CUs free up, so longest-first would give the first CUs all the
-  // long tiles: workgroups t, t + 256, t + 512, t + 768 share a CU, and a
-  // snake over blocks of 256 ranks (odd blocks reversed) gives every CU a
-  // mix of long and short tiles with about the same total.
+  __shared__ __attribute__((aligned(16))) float lds[InvTile::lds_floats];
   int t = blockIdx.x;
   if (gridDim.x <= 4 * 256) {
     const int blk = t >> 8, r = t & 255;
     t = (blk & 1) ? (blk << 8) + min(255, (int)gridDim.x - 1 - (blk << 8)) - r : t;
   }
-  const int major = t / (pairs * sb), rem = t % (pairs * sb);
-  const int p = rem / sb, minor = rem % sb;
-  const int rt = XSTEP ? sb - 1 - major : minor, ct = XSTEP ? minor : major;
-  const int a = 2 * s * p, b = a + s;
-  const int i0 = b + NB * rt, j0 = a + NB * ct;
-  if (i0 >= d) return;
-  const int ib = min(NB, d - i0);
-  const int k_lo = XSTEP ? 0 : NB * ct, k_hi = XSTEP ? min(NB * rt + NB, d - b) : s;
-  const float* Pb = XSTEP ? M + (int64_t)i0 * d + b : L + (int64_t)i0 * d + a;
-  const float* Qb = XSTEP ? Tb + (int64_t)b * d + j0 : M + (int64_t)a * d + j0;
-  f32x16 acc[Tile::FM][Tile::FN];
-  Tile::zero(acc);
-  typename Tile::PQRegs v;
-  auto fetch = [&](int k) __attribute__((always_inline)) {
-    const int kn = min(32, k_hi - k);
-    Tile::fetch_pq(v, Pb + k, d, ib, kn, Qb + (int64_t)k * d, d, kn, NB);
-  };
-  fetch(k_lo);
-  for (int k = k_lo; k < k_hi; k += 32) {
-    const int kn = min(32, k_hi - k);
-    if (k > k_lo) __syncthreads();
-    Tile::template stage_pq<XSTEP>(lds, v, ib, kn, kn, NB);
-    __syncthreads();
-    if (k + 32 < k_hi) fetch(k + 32);
-    Tile::mma(lds, acc);
-  }
-  float* C = (XSTEP ? M : Tb) + (int64_t)i0 * d + j0;
-  Tile::template store<false>(C, d, ib, NB, acc);
+  inv_item_tile(items, t, L, M, Tb, d, lds);
 }
 
 // U[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
@@ -884,6 +949,115 @@ int64_t sync_spin_limit() {
   }();
   return v;
 }
+
+namespace {
+
+// Flops of inverse tiles a factorization launch takes on, beyond its own
+// trailing-update passengers: about what the CUs its chain leaves idle do in
+// one panel's time.
+#ifndef INV_PASSENGER_FLOPS
+#define INV_PASSENGER_FLOPS 4.0e9
+#endif
+// The band launches (about 11 us at d = 4096) take short tiles only.
+#ifndef INV_BAND_FLOPS
+#define INV_BAND_FLOPS 0.5e9
+#endif
+constexpr int64_t INV_BAND_KMAX = 256;
+
+// Host bookkeeping of the inverse's tiles (inv_tile): which are done, and
+// which a launch may take given the columns of L that are final when it
+// starts.  Tiles of a step are handed out in order, so "done" is a count.
+class InvPlan {
+ public:
+  explicit InvPlan(int d) : d_(d) {
+    for (int s = NB; s < d; s *= 2) {
+      const int64_t pairs = ceil_div(d - s, 2 * s), sb = s / NB;
+      S_.push_back(s);
+      P_.push_back(pairs);
+      G_.push_back(pairs * sb * sb);
+    }
+    done_[0].assign(S_.size(), 0);
+    done_[1].assign(S_.size(), 0);
+  }
+  bool finished() const {
+    for (size_t li = 0; li < S_.size(); ++li)
+      if (done_[1][li] < G_[li]) return false;
+    return true;
+  }
+  // The tiles whose operands are complete when a launch starts with L's
+  // columns before cfin final, steps in level order (T before X), up to
+  // `budget` flops (all of them for a negative budget), tiles with K above
+  // kmax left out (one tile runs on one CU: a long one would hold up a short
+  // launch), and INV_ITEMS steps.  Tiles taken now count as done for later
+  // launches only.
+  InvItems take(int cfin, double budget, int64_t kmax = INT32_MAX) {
+    InvItems it{};
+    double used = 0.0;
+    std::vector<int64_t> add[2] = {std::vector<int64_t>(S_.size(), 0),
+                                   std::vector<int64_t>(S_.size(), 0)};
+    for (size_t li = 0; li < S_.size() && it.n < INV_ITEMS; ++li) {
+      for (int x = 0; x < 2 && it.n < INV_ITEMS; ++x) {
+        const int64_t g0 = done_[x][li];
+        int64_t c = 0;
+        while (g0 + c < G_[li] && ready((int)li, x, g0 + c, cfin)) {
+          const double f = tile_flops((int)li, x, g0 + c);
+          if (budget >= 0.0 && (used + f > budget || f > 2.0 * NB * NB * (double)kmax)) break;
+          used += f;
+          ++c;
+        }
+        if (c > 0) {
+          it.s[it.n] = S_[li];
+          it.x[it.n] = x;
+          it.g0[it.n] = (int)g0;
+          it.cnt[it.n] = (int)c;
+          ++it.n;
+          add[x][li] = c;
+        }
+      }
+    }
+    for (int x = 0; x < 2; ++x)
+      for (size_t li = 0; li < S_.size(); ++li) done_[x][li] += add[x][li];
+    return it;
+  }
+  static int count(const InvItems& it) {
+    int n = 0;
+    for (int i = 0; i < it.n; ++i) n += it.cnt[i];
+    return n;
+  }
+
+ private:
+  // A T tile reads L[b:e, a:b] and M[a:b, a:b]: L's columns before b final
+  // and every lower level's pairs inside [0, b) done.  An X tile reads M[b:e,
+  // b:e] and its pair's T tiles: columns before e final (the diagonal blocks'
+  // inverses come with the factorization) and lower levels done inside [0, e).
+  bool ready(int li, int x, int64_t g, int cfin) const {
+    const int64_t s = S_[li], sb = s / NB;
+    const int64_t p = g / (sb * sb);
+    const int64_t a = 2 * s * p, b = a + s, e = std::min<int64_t>(b + s, d_);
+    const int64_t need = x ? e : b;
+    if (need > cfin) return false;
+    if (x && done_[0][li] < (p + 1) * sb * sb) return false;
+    for (int lj = 0; lj < li; ++lj) {
+      const int64_t sj = S_[lj], sbj = sj / NB;
+      const int64_t pairs = std::min<int64_t>(P_[lj], ceil_div(need, 2 * sj));
+      if (done_[1][lj] < pairs * sbj * sbj) return false;
+    }
+    return true;
+  }
+  double tile_flops(int li, int x, int64_t g) const {
+    const int64_t s = S_[li], sb = s / NB;
+    const int64_t p = g / (sb * sb), lt = g % (sb * sb), major = lt / sb;
+    const int64_t b = 2 * s * p + s, e = std::min<int64_t>(b + s, d_);
+    const int64_t k = x ? std::min<int64_t>(NB * (sb - 1 - major) + NB, e - b) : s - NB * major;
+    return 2.0 * NB * NB * (double)std::max<int64_t>(k, 0);
+  }
+  int d_;
+  std::vector<int> S_;
+  std::vector<int64_t> P_, G_;
+  std::vector<int64_t> done_[2];
+};
+
+}  // namespace
 
 size_t prepare_workspace(int64_t d) {
   const size_t mat = align256((size_t)d * d * sizeof(float));
@@ -915,34 +1089,41 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t spin = sync_spin_limit();
+  InvPlan inv(d);
   for (int c0 = 0; c0 < d; c0 += PW) {
     const int rows = (int)ceil_div(d - c0, NB);
-    // passengers: the previous panel's update of the region from c0 + PW on
+    // passengers: the previous panel's update of the region from c0 + PW on,
+    // then the inverse's tiles that are ready, within what is left of the
+    // launch's passenger budget
     int rest = 0;
     if (c0 > 0 && c0 + PW < d) {
       const int nt = (int)ceil_div(d - c0 - PW, 128);
       rest = nt * (nt + 1) / 2;
     }
-    hipLaunchKernelGGL(chol_panel_kernel, dim3(rows + rest), dim3(256), 0, stream, w.A, w.M,
-                       w.Dinv, w.flags, d, c0, rows, c0 - PW, dev_status, spin);
+    const double trail = 2.0 * 128 * 128 * PW * rest;
+    const InvItems items = inv.take(c0, std::max(0.0, INV_PASSENGER_FLOPS - trail));
+    hipLaunchKernelGGL(chol_panel_kernel, dim3(rows + rest + InvPlan::count(items)), dim3(256), 0,
+                       stream, w.A, w.M, w.Dinv, w.flags, d, c0, rows, c0 - PW, rest, w.T, items,
+                       dev_status, spin);
     const int c1 = std::min(d, c0 + PW);
     if (c1 < d) {  // the band: the next panel's columns
       const int nr = (int)ceil_div(d - c1, 64);
       const int nbc = (int)ceil_div(std::min(d, c1 + PW) - c1, 64);
-      hipLaunchKernelGGL(chol_band_kernel, dim3(nr * nbc), dim3(256), 0, stream, w.A, d, c0, c1,
-                         nbc, (const int32_t*)dev_status);
+      const InvItems bitems = inv.take(c1, INV_BAND_FLOPS, INV_BAND_KMAX);
+      hipLaunchKernelGGL(chol_band_kernel, dim3(nr * nbc + InvPlan::count(bitems)), dim3(256), 0,
+                         stream, w.A, d, c0, c1, nbc, nr * nbc, w.M, w.T, bitems,
+                         (const int32_t*)dev_status);
     }
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  for (int s = NB; s < d; s *= 2) {
-    const int pairs = (int)ceil_div(d - s, 2 * s);  // pairs with b = a + s < d
-    const int sb = s / NB;
-    const unsigned tiles = (unsigned)(pairs * sb * sb);
-    hipLaunchKernelGGL(inv_level_kernel<false>, dim3(tiles), dim3(256), 0, stream,
-                       (const float*)w.A, w.M, w.T, d, s, pairs, (const int32_t*)dev_status);
-    hipLaunchKernelGGL(inv_level_kernel<true>, dim3(tiles), dim3(256), 0, stream,
-                       (const float*)w.A, w.M, w.T, d, s, pairs, (const int32_t*)dev_status);
+  // the rest of the inverse, a launch per round of ready tiles
+  while (!inv.finished()) {
+    const InvItems items = inv.take(d, -1.0);
+    const int n = InvPlan::count(items);
+    if (n == 0) return hipErrorUnknown;  // unreachable: with every column final a step is ready
+    hipLaunchKernelGGL(inv_items_kernel, dim3(n), dim3(256), 0, stream, (const float*)w.A, w.M,
+                       w.T, d, items, (const int32_t*)dev_status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
