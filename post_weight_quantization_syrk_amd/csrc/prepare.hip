@@ -30,6 +30,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "mfma_f32.h"
+#include "inv_plan.h"
 
 #include <algorithm>
 #include <cstdlib>
@@ -42,6 +43,7 @@ namespace {
 constexpr int NB = 64;
 constexpr int NJ = 4;                        // 64-column steps per panel
 constexpr int PW = NB * NJ;                  // panel width
+static_assert(NB == INV_NB && PW == INV_PW, "the inverse plan counts these tiles and panels");
 constexpr int FLAGS_PER_PANEL = NJ + NJ * NJ;  // diagonal-block flags, then block-column flags
 constexpr int SYNC_TIMEOUT = -1;             // dev_status when a bounded wait expires
 
@@ -637,11 +639,6 @@ constexpr size_t cmax(size_t a, size_t b) { return a > b ? a : b; }
 // latency-bound chain leaves idle), inv_items_kernel the rest.  The T regions
 // (and the X regions of M) of different pairs and levels are disjoint, and
 // every tile does the same arithmetic whichever launch runs it.
-constexpr int INV_ITEMS = 16;
-struct InvItems {  // tiles g0[i] .. g0[i] + cnt[i] - 1 of step (s[i], x[i]), in order
-  int n;
-  int s[INV_ITEMS], x[INV_ITEMS], g0[INV_ITEMS], cnt[INV_ITEMS];
-};
 using InvTile = MfmaTile<NB, NB, 32, false>;  // C = P Q with Q row-major
 
 template <bool XSTEP>
@@ -950,115 +947,6 @@ int64_t sync_spin_limit() {
   return v;
 }
 
-namespace {
-
-// Flops of inverse tiles a factorization launch takes on, beyond its own
-// trailing-update passengers: about what the CUs its chain leaves idle do in
-// one panel's time.
-#ifndef INV_PASSENGER_FLOPS
-#define INV_PASSENGER_FLOPS 4.0e9
-#endif
-// The band launches (about 11 us at d = 4096) take short tiles only.
-#ifndef INV_BAND_FLOPS
-#define INV_BAND_FLOPS 0.5e9
-#endif
-constexpr int64_t INV_BAND_KMAX = 256;
-
-// Host bookkeeping of the inverse's tiles (inv_tile): which are done, and
-// which a launch may take given the columns of L that are final when it
-// starts.  Tiles of a step are handed out in order, so "done" is a count.
-class InvPlan {
- public:
-  explicit InvPlan(int d) : d_(d) {
-    for (int s = NB; s < d; s *= 2) {
-      const int64_t pairs = ceil_div(d - s, 2 * s), sb = s / NB;
-      S_.push_back(s);
-      P_.push_back(pairs);
-      G_.push_back(pairs * sb * sb);
-    }
-    done_[0].assign(S_.size(), 0);
-    done_[1].assign(S_.size(), 0);
-  }
-  bool finished() const {
-    for (size_t li = 0; li < S_.size(); ++li)
-      if (done_[1][li] < G_[li]) return false;
-    return true;
-  }
-  // The tiles whose operands are complete when a launch starts with L's
-  // columns before cfin final, steps in level order (T before X), up to
-  // `budget` flops (all of them for a negative budget), tiles with K above
-  // kmax left out (one tile runs on one CU: a long one would hold up a short
-  // launch), and INV_ITEMS steps.  Tiles taken now count as done for later
-  // launches only.
-  InvItems take(int cfin, double budget, int64_t kmax = INT32_MAX) {
-    InvItems it{};
-    double used = 0.0;
-    std::vector<int64_t> add[2] = {std::vector<int64_t>(S_.size(), 0),
-                                   std::vector<int64_t>(S_.size(), 0)};
-    for (size_t li = 0; li < S_.size() && it.n < INV_ITEMS; ++li) {
-      for (int x = 0; x < 2 && it.n < INV_ITEMS; ++x) {
-        const int64_t g0 = done_[x][li];
-        int64_t c = 0;
-        while (g0 + c < G_[li] && ready((int)li, x, g0 + c, cfin)) {
-          const double f = tile_flops((int)li, x, g0 + c);
-          if (budget >= 0.0 && (used + f > budget || f > 2.0 * NB * NB * (double)kmax)) break;
-          used += f;
-          ++c;
-        }
-        if (c > 0) {
-          it.s[it.n] = S_[li];
-          it.x[it.n] = x;
-          it.g0[it.n] = (int)g0;
-          it.cnt[it.n] = (int)c;
-          ++it.n;
-          add[x][li] = c;
-        }
-      }
-    }
-    for (int x = 0; x < 2; ++x)
-      for (size_t li = 0; li < S_.size(); ++li) done_[x][li] += add[x][li];
-    return it;
-  }
-  static int count(const InvItems& it) {
-    int n = 0;
-    for (int i = 0; i < it.n; ++i) n += it.cnt[i];
-    return n;
-  }
-
- private:
-  // A T tile reads L[b:e, a:b] and M[a:b, a:b]: L's columns before b final
-  // and every lower level's pairs inside [0, b) done.  An X tile reads M[b:e,
-  // b:e] and its pair's T tiles: columns before e final (the diagonal blocks'
-  // inverses come with the factorization) and lower levels done inside [0, e).
-  bool ready(int li, int x, int64_t g, int cfin) const {
-    const int64_t s = S_[li], sb = s / NB;
-    const int64_t p = g / (sb * sb);
-    const int64_t a = 2 * s * p, b = a + s, e = std::min<int64_t>(b + s, d_);
-    const int64_t need = x ? e : b;
-    if (need > cfin) return false;
-    if (x && done_[0][li] < (p + 1) * sb * sb) return false;
-    for (int lj = 0; lj < li; ++lj) {
-      const int64_t sj = S_[lj], sbj = sj / NB;
-      const int64_t pairs = std::min<int64_t>(P_[lj], ceil_div(need, 2 * sj));
-      if (done_[1][lj] < pairs * sbj * sbj) return false;
-    }
-    return true;
-  }
-  double tile_flops(int li, int x, int64_t g) const {
-    const int64_t s = S_[li], sb = s / NB;
-    const int64_t p = g / (sb * sb), lt = g % (sb * sb), major = lt / sb;
-    const int64_t b = 2 * s * p + s, e = std::min<int64_t>(b + s, d_);
-    const int64_t k = x ? std::min<int64_t>(NB * (sb - 1 - major) + NB, e - b) : s - NB * major;
-    return 2.0 * NB * NB * (double)std::max<int64_t>(k, 0);
-  }
-  int d_;
-  std::vector<int> S_;
-  std::vector<int64_t> P_, G_;
-  std::vector<int64_t> done_[2];
-};
-
-}  // namespace
-
 size_t prepare_workspace(int64_t d) {
   const size_t mat = align256((size_t)d * d * sizeof(float));
   return 3 * mat + align256((size_t)((d + NB - 1) / NB) * NB * NB * sizeof(float)) +
@@ -1100,8 +988,7 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
       const int nt = (int)ceil_div(d - c0 - PW, 128);
       rest = nt * (nt + 1) / 2;
     }
-    const double trail = 2.0 * 128 * 128 * PW * rest;
-    const InvItems items = inv.take(c0, std::max(0.0, INV_PASSENGER_FLOPS - trail));
+    const InvItems items = inv_panel_items(inv, c0, rest);
     hipLaunchKernelGGL(chol_panel_kernel, dim3(rows + rest + InvPlan::count(items)), dim3(256), 0,
                        stream, w.A, w.M, w.Dinv, w.flags, d, c0, rows, c0 - PW, rest, w.T, items,
                        dev_status, spin);
@@ -1109,7 +996,7 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
     if (c1 < d) {  // the band: the next panel's columns
       const int nr = (int)ceil_div(d - c1, 64);
       const int nbc = (int)ceil_div(std::min(d, c1 + PW) - c1, 64);
-      const InvItems bitems = inv.take(c1, INV_BAND_FLOPS, INV_BAND_KMAX);
+      const InvItems bitems = inv_band_items(inv, c1);
       hipLaunchKernelGGL(chol_band_kernel, dim3(nr * nbc + InvPlan::count(bitems)), dim3(256), 0,
                          stream, w.A, d, c0, c1, nbc, nr * nbc, w.M, w.T, bitems,
                          (const int32_t*)dev_status);
