@@ -192,8 +192,7 @@ __global__ __launch_bounds__(256) void gidx_kernel(const int32_t* __restrict__ p
 }
 
 struct GroupParams {
-  float s, inv_s, hs, z;
-  float hs_lo;     // the largest float below hs (s/2)
+  float s, inv_s, hs, z;  // hs = s/2 (a normal float: s >= 2^-24)
   float zlo, zhi;  // -z and maxq - z: the range of code - z
 };
 
@@ -223,7 +222,6 @@ __device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi, i
   p.s = (float)s;
   p.inv_s = 1.0f / p.s;
   p.hs = 0.5f * p.s;
-  p.hs_lo = __int_as_float(__float_as_int(p.hs) - 1);  // hs >= 2^-25: a normal float
   p.z = z;
   p.zlo = -z;
   p.zhi = (float)maxq - z;
@@ -236,21 +234,23 @@ __device__ __forceinline__ GroupParams make_params(float lo_or_amax, float hi, i
 // 2^22, where that sum has unit spacing), which then holds q0's parity, and
 // subtracting it again gives q0 exactly.  r = x - q0 s is exact (q0 s has at
 // most 22 significant bits while |q0| <= 2^11, and |r| <= s keeps the
-// difference within x's precision), so comparing r with +-s/2 settles the
-// last unit; a tie (|r| = s/2) moves an odd q0 to its even neighbour, which
-// is the same as comparing against the float just below s/2 when q0 is odd.
-// Larger |y| (where r may be inexact) clamp to 0 or maxq whatever the last
-// unit.  The clamp is applied to code - z (to [-z, maxq - z], exact on these
-// small integers), and the error x - s (code - z) is formed with one
-// rounding.  Selects only: this sits on the column loop's dependency chain.
-// Returns the error; the code goes to *code.
+// difference within x's precision), so comparing |r| with s/2 settles the
+// last unit: q0 moves one step towards r's sign when |r| > s/2; a tie (|r| =
+// s/2) moves an odd q0 to its even neighbour, which is the same as comparing
+// against the float just below s/2 (its bit pattern minus one) when q0 is
+// odd.  Larger |y| (where r may be inexact) clamp to 0 or maxq whatever the
+// last unit.  The clamp is applied to code - z (to [-z, maxq - z], exact on
+// these small integers), and the error x - s (code - z) is formed with one
+// rounding.  Selects and integer arithmetic only, with a single decision on
+// |r|: this sits on the column loop's dependency chain.  Returns the error;
+// the code goes to *code.
 __device__ __forceinline__ float quantize_step(float x, const GroupParams& p, float* code) {
   constexpr float MAGIC = 12582912.0f;  // 1.5 * 2^23
   const float m = fmaf(x, p.inv_s, MAGIC);
   const float q0 = m - MAGIC;
-  const float t = (__float_as_uint(m) & 1u) ? p.hs_lo : p.hs;
+  const float t = __int_as_float(__float_as_int(p.hs) - (int)(__float_as_uint(m) & 1u));
   const float r = fmaf(-q0, p.s, x);
-  const float v = (r > t) ? q0 + 1.0f : ((r < -t) ? q0 - 1.0f : q0);
+  const float v = (fabsf(r) > t) ? q0 + copysignf(1.0f, r) : q0;
   const float cz = __builtin_amdgcn_fmed3f(v, p.zlo, p.zhi);
   *code = cz + p.z;
   return fmaf(-p.s, cz, x);
@@ -483,7 +483,6 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     gp.s = scales[rr];
     gp.inv_s = 1.0f / gp.s;
     gp.hs = 0.5f * gp.s;
-    gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
     gp.z = zeros[rr];
     gp.zlo = -gp.z;
     gp.zhi = maxq - gp.z;
@@ -528,7 +527,6 @@ __global__ __launch_bounds__(256) void colloop_kernel(
       gp.zlo = -nz;
       gp.zhi = maxq - nz;
       gp.hs = 0.5f * gp.s;
-      gp.hs_lo = __int_as_float(__float_as_int(gp.hs) - 1);
       if constexpr (j + 1 < QB) {
         const int e = (tid / LPR) * QB + j + 1;
         ns = sps[e];
