@@ -419,27 +419,43 @@ __global__ __launch_bounds__(256) void ublock_kernel(const float* __restrict__ U
 // staged in LDS per row and column at the start.  Otherwise each group's
 // parameters are set at its first column from the current values and
 // written to scales/zeros.
+//
+// One launch takes a group of nblk blocks from column g0 on.  The rows of a
+// workgroup are its own for the whole group, so after each block's column
+// loop it applies that block's scaled errors to the group's later blocks
+// itself (the near update W[rows, later] -= delta U[block, later], the
+// operands and products of the trailing update: the errors' three bf16 parts
+// staged in LDS, U^T's parts read from memory, six part products per product
+// on the matrix cores, summed from zero and subtracted once), and its next
+// block starts from those values: no launch per block and none for the near
+// updates.
+constexpr int EAP = QB + 8;  // LDS pitch (bf16) of the staged error parts
 template <bool STATIC, int LPR>
 __global__ __launch_bounds__(256) void colloop_kernel(
     float* __restrict__ Wc, uint16_t* __restrict__ E3, int64_t se, const float* __restrict__ Ub,
-    const float* __restrict__ Uinv, int64_t d_out, int64_t d_in, int64_t b0, QSpec q,
-    uint8_t* __restrict__ codes,
+    const float* __restrict__ Uinv, const uint16_t* __restrict__ Ut3, int64_t su, int64_t d_out,
+    int64_t d_in, int64_t g0, int nblk, QSpec q, uint8_t* __restrict__ codes,
     float* __restrict__ scales, float* __restrict__ zeros, float* __restrict__ loss_rows,
     const int32_t* __restrict__ perm) {
   constexpr int CPL = QB / LPR;   // columns per lane
   constexpr int RPB = 256 / LPR;  // rows per workgroup
-  static_assert(CPL == 4 || CPL == 8, "16 or 32 lanes per row");
+  static_assert(CPL == 8 && RPB == 16, "16 lanes per row, 16 rows per workgroup");
   __shared__ __attribute__((aligned(16))) float us[QB * UPITCH];
   __shared__ float invd[QB];
+  __shared__ __attribute__((aligned(16))) uint16_t ea[3][RPB * EAP];  // the block's error parts
   __shared__ float sps[STATIC ? RPB * QB : 1], spi[STATIC ? RPB * QB : 1],
       spz[STATIC ? RPB * QB : 1];
   const int tid = threadIdx.x;
-  const int bw = (int)min<int64_t>(QB, d_in - b0);
   const int c = tid & (LPR - 1);  // lane within the row group
-  const int64_t row = (int64_t)blockIdx.x * RPB + tid / LPR;
+  const int rl = tid / LPR;       // row within the workgroup
+  const int64_t row = (int64_t)blockIdx.x * RPB + rl;
   const bool live = row < d_out;
   const int64_t rr = live ? row : 0;
   const float maxq = (float)q.maxq;
+  for (int jb = 0; jb < nblk; ++jb) {
+  const int64_t b0 = g0 + (int64_t)jb * QB;
+  const int bw = (int)min<int64_t>(QB, d_in - b0);
+  if (jb > 0) __syncthreads();  // the previous block's near updates are in Wc, us is free
   float w[CPL];
   {
     // this lane's CPL columns of the row (unconditional loads, masked after)
@@ -588,11 +604,11 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     loss = fmaf(er[i], er[i], loss);
   }
   loss = row_sum<LPR>(loss);
-  if (!live) return;
   // codes and scaled errors of this lane's columns: the codes as one store
   // of CPL bytes when d_in is a multiple of CPL and codes is aligned to it;
   // the errors split into their three bf16 parts, one store of CPL values per
   // part (they lie in one k chunk: b0 and CPL c are multiples of CPL)
+  if (live) {
   uint8_t* cdst = codes + rr * d_in + b0 + CPL * c;
   const int64_t kabs = b0 + CPL * c;
   uint16_t* edst = E3 + (kabs / KC) * 3 * se + rr * KC + kabs % KC;
@@ -615,6 +631,11 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     uint32_t hw[CPL / 2], mw[CPL / 2], lw[CPL / 2];
 #pragma unroll
     for (int t = 0; t < CPL / 2; ++t) hw[t] = split_pair(er[2 * t], er[2 * t + 1], mw[t], lw[t]);
+    if (jb + 1 < nblk) {  // the parts again, for this workgroup's near updates
+      *(uint4*)(&ea[0][rl * EAP + CPL * c]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+      *(uint4*)(&ea[1][rl * EAP + CPL * c]) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
+      *(uint4*)(&ea[2][rl * EAP + CPL * c]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+    }
     if constexpr (CPL == 8) {
       *(uint4*)edst = make_uint4(hw[0], hw[1], hw[2], hw[3]);
       *(uint4*)(edst + se) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
@@ -634,7 +655,86 @@ __global__ __launch_bounds__(256) void colloop_kernel(
         edst[2 * se + i] = lo;
       }
   }
-  if (loss_rows && c == 0) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
+  }  // live
+  if (loss_rows && c == 0 && live) loss_rows[rr] = (b0 == 0 ? 0.0f : loss_rows[rr]) + loss;
+  if (jb + 1 < nblk) {
+    // Rows past d_out hold whatever LDS held: a product keeps rows apart
+    // and those rows are never stored.  Every block but the matrix's last is
+    // full, so the staged parts cover all 128 columns.
+    __syncthreads();  // ea complete
+    const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+    const bool arow = l32 < RPB;  // MFMA rows 16..31 are zero padding
+    for (int jt = jb + 1; jt < nblk; ++jt) {
+      const int64_t bt = g0 + (int64_t)jt * QB;
+      const int btw = (int)min<int64_t>(QB, d_in - bt);
+      // wave: target columns bt + 32 wave .. + 31; lane: column l32, k 8 h .. + 7 of a step
+      const int64_t ncol = bt + min(32 * wave + l32, btw - 1);
+      f32x16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
+      uint4 bq[2][2][3];  // [buffer][16-k step][part]
+      auto bload = [&](uint4 (&bb)[2][3], int kc) __attribute__((always_inline)) {
+        const uint16_t* pb = Ut3 + ((b0 + kc) / KC) * 3 * su + ncol * KC + 8 * h;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int pt = 0; pt < 3; ++pt) bb[ks][pt] = *(const uint4*)(pb + pt * su + 16 * ks);
+      };
+      auto prod = [&](const uint4 (&bb)[2][3], int kc) __attribute__((always_inline)) {
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          const int ko = kc + 16 * ks + 8 * h;
+          uint4 av[3];
+#pragma unroll
+          for (int pt = 0; pt < 3; ++pt)
+            av[pt] = arow ? *(const uint4*)(&ea[pt][l32 * EAP + ko]) : make_uint4(0, 0, 0, 0);
+          const bf16x8 ah = __builtin_bit_cast(bf16x8, av[0]);
+          const bf16x8 am = __builtin_bit_cast(bf16x8, av[1]);
+          const bf16x8 al = __builtin_bit_cast(bf16x8, av[2]);
+          const bf16x8 bh = __builtin_bit_cast(bf16x8, bb[ks][0]);
+          const bf16x8 bm = __builtin_bit_cast(bf16x8, bb[ks][1]);
+          const bf16x8 bl = __builtin_bit_cast(bf16x8, bb[ks][2]);
+          // the six part products, smallest first: l h, h l, m m, m h, h m, h h
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bl, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bm, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am, bh, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bm, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
+        }
+      };
+      // four 32-k chunks, the next one's U^T parts loaded during the products
+      bload(bq[0], 0);
+      __builtin_amdgcn_sched_barrier(0);
+      bload(bq[1], 32);
+      __builtin_amdgcn_sched_barrier(0);
+      prod(bq[0], 0);
+      bload(bq[0], 64);
+      __builtin_amdgcn_sched_barrier(0);
+      prod(bq[1], 32);
+      bload(bq[1], 96);
+      __builtin_amdgcn_sched_barrier(0);
+      prod(bq[0], 64);
+      prod(bq[1], 96);
+      // registers 0..7 hold the 16 real rows: 8 (r / 4) + 4 h + r % 4
+      const int cl = 32 * wave + l32;
+      if (cl < btw) {
+        float* col = Wc + bt + cl;
+        float old[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t gr = (int64_t)blockIdx.x * RPB + 8 * (r >> 2) + 4 * h + (r & 3);
+          old[r] = col[min(gr, d_out - 1) * d_in];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const int64_t gr = (int64_t)blockIdx.x * RPB + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (gr < d_out) col[gr * d_in] = old[r] - acc[r];
+        }
+      }
+    }
+  }
+  }  // blocks of the group
 }
 
 // Wc[:, n0:n1] -= delta[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
@@ -1023,25 +1123,16 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   for (int64_t g0 = 0; g0 < nb; g0 += QG) {
     const int64_t gend = std::min<int64_t>(nb, g0 + QG);
     const int64_t gcol = std::min<int64_t>(d_in, gend * QB);  // first column after the group
-    for (int64_t b = g0; b < gend; ++b) {
-      const int64_t b0 = b * QB;
-      if (stat)
-        hipLaunchKernelGGL((colloop_kernel<true, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
-                           w.E3, w.se, w.Ub, w.Uinv, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows,
-                           perm);
-      else
-        hipLaunchKernelGGL((colloop_kernel<false, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
-                           w.E3, w.se, w.Ub, w.Uinv, d_out, d_in, b0, q, codes_k, scales, zeros, loss_rows,
-                           perm);
-      const int64_t n0 = b0 + QB;
-      if (b + 1 < gend) {  // blocks before the group's last are full
-        const int64_t tiles = ceil_div(d_out, 64) * ceil_div(gcol - n0, 64);
-        hipLaunchKernelGGL((trailing3_kernel<64, 64>), dim3((unsigned)(8 * ceil_div(tiles, 8))),
-                           dim3(256), 0, stream,
-                           w.Wc, (const uint16_t*)w.E3, w.se, (const uint16_t*)w.Ut3, w.su, d_out,
-                           d_in, b0, QB, n0, gcol);
-      }
-    }
+    // the group's column loops and their near updates, one launch
+    const int nblk = (int)(gend - g0);
+    if (stat)
+      hipLaunchKernelGGL((colloop_kernel<true, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
+                         w.E3, w.se, w.Ub, w.Uinv, (const uint16_t*)w.Ut3, w.su, d_out, d_in,
+                         g0 * QB, nblk, q, codes_k, scales, zeros, loss_rows, perm);
+    else
+      hipLaunchKernelGGL((colloop_kernel<false, CL_LPR>), dim3(rgrid), dim3(256), 0, stream, w.Wc,
+                         w.E3, w.se, w.Ub, w.Uinv, (const uint16_t*)w.Ut3, w.su, d_out, d_in,
+                         g0 * QB, nblk, q, codes_k, scales, zeros, loss_rows, perm);
     if (gcol < d_in) {  // every block of the group is full
       // 128 x 128 tiles (half the LDS bytes per product, two waves per SIMD)
       // when the launch still has enough of them to fill the chip several
