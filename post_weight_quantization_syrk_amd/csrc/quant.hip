@@ -661,25 +661,33 @@ __global__ __launch_bounds__(256) void colloop_kernel(
     // Rows past d_out hold whatever LDS held: a product keeps rows apart
     // and those rows are never stored.  Every block but the matrix's last is
     // full, so the staged parts cover all 128 columns.
-    __syncthreads();  // ea complete
     const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
     const bool arow = l32 < RPB;  // MFMA rows 16..31 are zero padding
+    // U^T parts of target block jt, 32-k chunk kc: this lane's column and k
+    auto bload = [&](uint4 (&bb)[2][3], int jt, int kc) __attribute__((always_inline)) {
+      const int64_t bt = g0 + (int64_t)jt * QB;
+      const int64_t ncol = bt + min(32 * wave + l32, (int)min<int64_t>(QB, d_in - bt) - 1);
+      const uint16_t* pb = Ut3 + ((b0 + kc) / KC) * 3 * su + ncol * KC + 8 * h;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int pt = 0; pt < 3; ++pt) bb[ks][pt] = *(const uint4*)(pb + pt * su + 16 * ks);
+    };
+    uint4 bq[2][2][3];  // [buffer][16-k step][part]
+    // the first target's first two chunks (every later target's come at the
+    // end of the one before, so each target starts with them in flight)
+    bload(bq[0], jb + 1, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    bload(bq[1], jb + 1, 32);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();  // ea complete
     for (int jt = jb + 1; jt < nblk; ++jt) {
       const int64_t bt = g0 + (int64_t)jt * QB;
       const int btw = (int)min<int64_t>(QB, d_in - bt);
-      // wave: target columns bt + 32 wave .. + 31; lane: column l32, k 8 h .. + 7 of a step
-      const int64_t ncol = bt + min(32 * wave + l32, btw - 1);
+      const int jn = min(jt + 1, nblk - 1);  // the next target (the last loads itself again)
       f32x16 acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-      uint4 bq[2][2][3];  // [buffer][16-k step][part]
-      auto bload = [&](uint4 (&bb)[2][3], int kc) __attribute__((always_inline)) {
-        const uint16_t* pb = Ut3 + ((b0 + kc) / KC) * 3 * su + ncol * KC + 8 * h;
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-          for (int pt = 0; pt < 3; ++pt) bb[ks][pt] = *(const uint4*)(pb + pt * su + 16 * ks);
-      };
       auto prod = [&](const uint4 (&bb)[2][3], int kc) __attribute__((always_inline)) {
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -703,29 +711,32 @@ __global__ __launch_bounds__(256) void colloop_kernel(
           acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, bh, acc, 0, 0, 0);
         }
       };
-      // four 32-k chunks, the next one's U^T parts loaded during the products
-      bload(bq[0], 0);
+      // the target's current values (registers 0..7 of the product hold the
+      // 16 real rows, 8 (r / 4) + 4 h + r % 4), read before the products
+      const int cl = 32 * wave + l32;
+      float* col = Wc + bt + min(cl, btw - 1);
+      float old[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int64_t gr = (int64_t)blockIdx.x * RPB + 8 * (r >> 2) + 4 * h + (r & 3);
+        old[r] = col[min(gr, d_out - 1) * d_in];
+      }
       __builtin_amdgcn_sched_barrier(0);
-      bload(bq[1], 32);
-      __builtin_amdgcn_sched_barrier(0);
+      // four 32-k chunks, each next one's U^T parts loaded during the products,
+      // then the next target's first two
       prod(bq[0], 0);
-      bload(bq[0], 64);
+      bload(bq[0], jt, 64);
       __builtin_amdgcn_sched_barrier(0);
       prod(bq[1], 32);
-      bload(bq[1], 96);
+      bload(bq[1], jt, 96);
       __builtin_amdgcn_sched_barrier(0);
       prod(bq[0], 64);
+      bload(bq[0], jn, 0);
+      __builtin_amdgcn_sched_barrier(0);
       prod(bq[1], 96);
-      // registers 0..7 hold the 16 real rows: 8 (r / 4) + 4 h + r % 4
-      const int cl = 32 * wave + l32;
+      bload(bq[1], jn, 32);
+      __builtin_amdgcn_sched_barrier(0);
       if (cl < btw) {
-        float* col = Wc + bt + cl;
-        float old[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-          const int64_t gr = (int64_t)blockIdx.x * RPB + 8 * (r >> 2) + 4 * h + (r & 3);
-          old[r] = col[min(gr, d_out - 1) * d_in];
-        }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
           const int64_t gr = (int64_t)blockIdx.x * RPB + 8 * (r >> 2) + 4 * h + (r & 3);
