@@ -614,8 +614,9 @@ def main():
     }
     upd_tflops = (syrk_flops + trail_flops) / ((stage_ms["hessian"] + stage_ms["quantize"]) / 1e3) / 1e12
     rl = roofline_bound_ms(wl)
-    # the far trailing update's own rate: its kernels (operand split + far
-    # updates) timed by the profiler over one more quantize call
+    # the far trailing update's own rate: its kernels (operand split, which
+    # shares a launch with the column loop's diagonal blocks, + far updates)
+    # timed by the profiler over one more quantize call
     trail_ms = None
     if not order and d_in > wl.block and not args.no_profiler:
         try:
@@ -624,15 +625,16 @@ def main():
                                                  group_size=wl.group_size, sym=wl.sym,
                                                  block=wl.block, codes=codes, scales=scales,
                                                  zeros=zeros, want_loss=False, ws=ws_q),
-                ("trailing3_kernel", "split_ut_kernel"))
+                ("trailing3_kernel", "uprep_kernel"))
         except Exception as e:  # the profiler is optional here
             log(f"trailing kernels not timed: {e}")
     trailing = None
     if trail_ms:
         far_flops = far_update_flops(d_out, d_in, wl.block)
         t_tf = far_flops / (trail_ms / 1e3) / 1e12
-        trailing = {"kernels": "split_ut_kernel + trailing3_kernel (far updates; the near updates "
-                               "within a group run inside colloop_kernel)",
+        trailing = {"kernels": "uprep_kernel (U^T split into parts, with the column loop's "
+                               "diagonal blocks of U) + trailing3_kernel (far updates; the near "
+                               "updates within a group run inside colloop_kernel)",
                     "ms": round(trail_ms, 4), "algorithmic_flops": far_flops,
                     "achieved": round(t_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(t_tf / PEAK_BF16_TFLOPS, 4),

@@ -393,16 +393,16 @@ __device__ __forceinline__ uint32_t split_pair(float x0, float x1, uint32_t& mid
 // then its unscaled error x - what times the scaled row, and neither the
 // division nor its read sits on the chain from one column to the next.  One
 // workgroup per block; thread t does half t % 2 of row t / 2.
-__global__ __launch_bounds__(256) void ublock_kernel(const float* __restrict__ U, int64_t d_in,
-                                                     float* __restrict__ Ub,
-                                                     float* __restrict__ Uinv) {
-  const int64_t b0 = (int64_t)blockIdx.x * QB;
+__device__ __forceinline__ void ublock_block(const float* __restrict__ U, int64_t d_in,
+                                             float* __restrict__ Ub, float* __restrict__ Uinv,
+                                             int blk) {
+  const int64_t b0 = (int64_t)blk * QB;
   const int bw = (int)min<int64_t>(QB, d_in - b0);
   const int tid = threadIdx.x, r = tid >> 1, h = tid & 1;
   const float diag = (r < bw) ? U[(b0 + r) * d_in + b0 + r] : 1.0f;
   const float sc = 1.0f / diag;
   if (h == 0) Uinv[b0 + r] = sc;
-  float* dst = Ub + (int64_t)blockIdx.x * QB * QB + r * QB + 64 * h;
+  float* dst = Ub + (int64_t)blk * QB * QB + r * QB + 64 * h;
   const float* src = U + (b0 + min(r, bw - 1)) * d_in + b0;
 #pragma unroll 4
   for (int i = 0; i < 64; ++i) {
@@ -773,13 +773,13 @@ constexpr int T3P = T3K + 8;      // LDS row pitch (bf16 elements): 80 bytes
 // p, row n, position k % 32, for the 64 x 64 tiles (k block kt, n block nt)
 // with kt <= nt (the update reads k < n only).  The tile goes through LDS so
 // that the loads of U's rows and the stores of U^T's rows are contiguous.
-__global__ __launch_bounds__(256) void split_ut_kernel(const float* __restrict__ U, int64_t d_in,
-                                                       uint16_t* __restrict__ Ut3, int64_t su) {
+__device__ __forceinline__ void split_ut_tile(const float* __restrict__ U, int64_t d_in,
+                                              uint16_t* __restrict__ Ut3, int64_t su, int tile) {
   __shared__ float t[64][65];
-  int nt = (int)((sqrtf(8.0f * (float)blockIdx.x + 1.0f) - 1.0f) * 0.5f);
-  while ((nt + 1) * (nt + 2) / 2 <= (int)blockIdx.x) ++nt;
-  while (nt * (nt + 1) / 2 > (int)blockIdx.x) --nt;
-  const int kt = (int)blockIdx.x - nt * (nt + 1) / 2;
+  int nt = (int)((sqrtf(8.0f * (float)tile + 1.0f) - 1.0f) * 0.5f);
+  while ((nt + 1) * (nt + 2) / 2 <= tile) ++nt;
+  while (nt * (nt + 1) / 2 > tile) --nt;
+  const int kt = tile - nt * (nt + 1) / 2;
   const int64_t k0 = 64 * (int64_t)kt, n0 = 64 * (int64_t)nt;
   const int tid = threadIdx.x;
   for (int e = tid; e < 64 * 64; e += 256) {
@@ -804,6 +804,20 @@ __global__ __launch_bounds__(256) void split_ut_kernel(const float* __restrict__
     *(uint4*)(dst + su + 8 * h) = make_uint4(mw[0], mw[1], mw[2], mw[3]);
     *(uint4*)(dst + 2 * su + 8 * h) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
   }
+}
+
+// Once per call, both from U: the column loop's scaled diagonal blocks
+// (workgroups 0 .. nblk - 1, first, as they take longest) and U^T's bf16
+// parts for the trailing updates (the rest), in one launch.
+__global__ __launch_bounds__(256) void uprep_kernel(const float* __restrict__ U, int64_t d_in,
+                                                    float* __restrict__ Ub,
+                                                    float* __restrict__ Uinv,
+                                                    uint16_t* __restrict__ Ut3, int64_t su,
+                                                    int nblk) {
+  if ((int)blockIdx.x < nblk)
+    ublock_block(U, d_in, Ub, Uinv, (int)blockIdx.x);
+  else
+    split_ut_tile(U, d_in, Ut3, su, (int)blockIdx.x - nblk);
 }
 
 // The launches give b0 and kb multiples of 32 (whole chunks) and n0 a
@@ -1121,14 +1135,14 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // K = 128 QG), so the bulk of W is read and written once per group.
   const unsigned rgrid = (unsigned)ceil_div(d_out, 256 / CL_LPR);
   static_assert(QB % T3K == 0, "trailing updates take whole chunks");
-  hipLaunchKernelGGL(ublock_kernel, dim3((unsigned)n_blocks(d_in)), dim3(256), 0, stream, U, d_in,
-                     w.Ub, w.Uinv);
-  // U^T in parts, for every trailing update of this call (only the 64 x 64
-  // tiles on or above U's diagonal)
-  if (d_in > QB) {
+  // the scaled diagonal blocks of U, and U^T in parts for every trailing
+  // update of this call (only the 64 x 64 tiles on or above U's diagonal)
+  {
     const int64_t nt = ceil_div(d_in, 64);
-    hipLaunchKernelGGL(split_ut_kernel, dim3((unsigned)(nt * (nt + 1) / 2)), dim3(256), 0, stream,
-                       U, d_in, w.Ut3, w.su);
+    const int nsplit = (d_in > QB) ? (int)(nt * (nt + 1) / 2) : 0;
+    const int nblk_u = (int)n_blocks(d_in);
+    hipLaunchKernelGGL(uprep_kernel, dim3((unsigned)(nblk_u + nsplit)), dim3(256), 0, stream, U,
+                       d_in, w.Ub, w.Uinv, w.Ut3, w.su, nblk_u);
   }
   const int64_t nb = ceil_div(d_in, QB);
   for (int64_t g0 = 0; g0 < nb; g0 += QG) {
