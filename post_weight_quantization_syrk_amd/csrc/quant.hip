@@ -99,14 +99,14 @@ __device__ __forceinline__ double f64_to_f16_value(double x) {
 // Wc = W as fp32, dead columns zeroed.  With vec (d_in % 8 == 0 and W
 // 16-byte aligned) each thread converts 8 consecutive elements of a row:
 // one 16-byte load of bf16 (or two of fp32) and two 16-byte stores.
-__global__ __launch_bounds__(256) void qinit_kernel(const void* __restrict__ W, int w_dtype,
-                                                    int64_t d_out, int64_t d_in,
-                                                    const uint8_t* __restrict__ dead,
-                                                    float* __restrict__ Wc, int vec) {
+// (Workgroup bid of nbid doing this part of a launch.)
+__device__ __forceinline__ void qinit_part(const void* __restrict__ W, int w_dtype, int64_t d_out,
+                                           int64_t d_in, const uint8_t* __restrict__ dead,
+                                           float* __restrict__ Wc, int vec, int bid, int nbid) {
   const int64_t total = d_out * d_in;
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const int64_t stride = (int64_t)nbid * 256;
   if (vec) {
-    for (int64_t e8 = (int64_t)blockIdx.x * 256 + threadIdx.x; e8 < total / 8; e8 += stride) {
+    for (int64_t e8 = (int64_t)bid * 256 + threadIdx.x; e8 < total / 8; e8 += stride) {
       const int64_t c = (e8 * 8) % d_in;
       float v[8];
       if (w_dtype == 0) {
@@ -132,12 +132,22 @@ __global__ __launch_bounds__(256) void qinit_kernel(const void* __restrict__ W, 
     }
     return;
   }
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += stride) {
+  for (int64_t e = (int64_t)bid * 256 + threadIdx.x; e < total; e += stride) {
     const int64_t c = e % d_in;
     float v = (w_dtype == 0) ? bf16_bits_to_float(((const uint16_t*)W)[e]) : ((const float*)W)[e];
     if (dead && dead[c]) v = 0.0f;
     Wc[e] = v;
   }
+}
+__global__ __launch_bounds__(256) void qinit_kernel(const void* __restrict__ W, int w_dtype,
+                                                    int64_t d_out, int64_t d_in,
+                                                    const uint8_t* __restrict__ dead,
+                                                    float* __restrict__ Wc, int vec) {
+  qinit_part(W, w_dtype, d_out, d_in, dead, Wc, vec, (int)blockIdx.x, (int)gridDim.x);
+}
+inline unsigned qinit_grid(int64_t rows, int64_t d_in, int vec) {
+  const int64_t total = rows * d_in;
+  return (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
 }
 
 // Column order ([P1] GPTQ 的高级技巧, 激活排序): Wc[:, k] = W[:, perm[k]] as fp32,
@@ -806,18 +816,25 @@ __device__ __forceinline__ void split_ut_tile(const float* __restrict__ U, int64
   }
 }
 
-// Once per call, both from U: the column loop's scaled diagonal blocks
-// (workgroups 0 .. nblk - 1, first, as they take longest) and U^T's bf16
-// parts for the trailing updates (the rest), in one launch.
+// Once per call, in one launch: the column loop's scaled diagonal blocks of
+// U (workgroups 0 .. nblk - 1, first, as they take longest), U^T's bf16 parts
+// for the trailing updates (the next nsplit), and, when nq > 0, the working
+// copy Wc of W (the last nq: qinit_part).
 __global__ __launch_bounds__(256) void uprep_kernel(const float* __restrict__ U, int64_t d_in,
                                                     float* __restrict__ Ub,
                                                     float* __restrict__ Uinv,
                                                     uint16_t* __restrict__ Ut3, int64_t su,
-                                                    int nblk) {
-  if ((int)blockIdx.x < nblk)
-    ublock_block(U, d_in, Ub, Uinv, (int)blockIdx.x);
+                                                    int nblk, int nsplit, const void* W,
+                                                    int w_dtype, int64_t d_out,
+                                                    const uint8_t* __restrict__ dead,
+                                                    float* __restrict__ Wc, int vec, int nq) {
+  const int b = (int)blockIdx.x;
+  if (b < nblk)
+    ublock_block(U, d_in, Ub, Uinv, b);
+  else if (b < nblk + nsplit)
+    split_ut_tile(U, d_in, Ut3, su, b - nblk);
   else
-    split_ut_tile(U, d_in, Ut3, su, (int)blockIdx.x - nblk);
+    qinit_part(W, w_dtype, d_out, d_in, dead, Wc, vec, b - nblk - nsplit, nq);
 }
 
 // The launches give b0 and kb multiples of 32 (whole chunks) and n0 a
@@ -1096,22 +1113,34 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // the workspace; they are put back in natural order at the end
   uint8_t* codes_k = perm ? (uint8_t*)ws + quantize_workspace(d_out, d_in, QB) : codes;
   const dim3 pgrid((unsigned)ceil_div(d_in, 256), (unsigned)std::min<int64_t>(d_out, 1024));
+  // One matrix in natural order: its working copy is made in the same launch
+  // as U's preparation (below); otherwise here.
+  const bool q_merged = !perm && src.count == 1 && d_out > 0;
+  const int q_vec = (d_in % 8 == 0) && ((uintptr_t)W % 16 == 0);
   if (perm) {
     hipLaunchKernelGGL(qinit_perm_kernel, pgrid, dim3(256), 0, stream, W, w_dtype, d_out, d_in,
                        dead, perm, w.Wc);
-  } else {
+  } else if (!q_merged) {
     int64_t r0 = 0;
     for (int i = 0; i < src.count; ++i) {
       const int64_t rows = src.rows[i];
       if (rows == 0) continue;
-      const int64_t total = rows * d_in;
       const int vec = (d_in % 8 == 0) && ((uintptr_t)src.ptrs[i] % 16 == 0);
-      const unsigned grid =
-          (unsigned)std::min<int64_t>(ceil_div(vec ? total / 8 : total, 256), 65536);
-      hipLaunchKernelGGL(qinit_kernel, dim3(grid), dim3(256), 0, stream, src.ptrs[i], w_dtype,
-                         rows, d_in, dead, w.Wc + r0 * d_in, vec);
+      hipLaunchKernelGGL(qinit_kernel, dim3(qinit_grid(rows, d_in, vec)), dim3(256), 0, stream,
+                         src.ptrs[i], w_dtype, rows, d_in, dead, w.Wc + r0 * d_in, vec);
       r0 += rows;
     }
+  }
+  // the scaled diagonal blocks of U, and U^T in parts for every trailing
+  // update of this call (only the 64 x 64 tiles on or above U's diagonal)
+  {
+    const int64_t nt = ceil_div(d_in, 64);
+    const int nsplit = (d_in > QB) ? (int)(nt * (nt + 1) / 2) : 0;
+    const int nblk_u = (int)n_blocks(d_in);
+    const int nq = q_merged ? (int)qinit_grid(d_out, d_in, q_vec) : 0;
+    hipLaunchKernelGGL(uprep_kernel, dim3((unsigned)(nblk_u + nsplit + nq)), dim3(256), 0, stream,
+                       U, d_in, w.Ub, w.Uinv, w.Ut3, w.su, nblk_u, nsplit, W, w_dtype, d_out,
+                       dead, w.Wc, q_vec, nq);
   }
   QSpec q;
   q.maxq = (1 << bits) - 1;
@@ -1135,15 +1164,7 @@ hipError_t quantize_core(const WSource& src, int w_dtype, int64_t d_out, int64_t
   // K = 128 QG), so the bulk of W is read and written once per group.
   const unsigned rgrid = (unsigned)ceil_div(d_out, 256 / CL_LPR);
   static_assert(QB % T3K == 0, "trailing updates take whole chunks");
-  // the scaled diagonal blocks of U, and U^T in parts for every trailing
-  // update of this call (only the 64 x 64 tiles on or above U's diagonal)
-  {
-    const int64_t nt = ceil_div(d_in, 64);
-    const int nsplit = (d_in > QB) ? (int)(nt * (nt + 1) / 2) : 0;
-    const int nblk_u = (int)n_blocks(d_in);
-    hipLaunchKernelGGL(uprep_kernel, dim3((unsigned)(nblk_u + nsplit)), dim3(256), 0, stream, U,
-                       d_in, w.Ub, w.Uinv, w.Ut3, w.su, nblk_u);
-  }
+
   const int64_t nb = ceil_div(d_in, QB);
   for (int64_t g0 = 0; g0 < nb; g0 += QG) {
     const int64_t gend = std::min<int64_t>(nb, g0 + QG);
