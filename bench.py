@@ -633,8 +633,9 @@ def main():
         far_flops = far_update_flops(d_out, d_in, wl.block)
         t_tf = far_flops / (trail_ms / 1e3) / 1e12
         trailing = {"kernels": "uprep_kernel (U^T split into parts, with the column loop's "
-                               "diagonal blocks of U) + trailing3_kernel (far updates; the near "
-                               "updates within a group run inside colloop_kernel)",
+                               "diagonal blocks of U and W's working copy in the same launch) "
+                               "+ trailing3_kernel (far updates; the near updates within a "
+                               "group run inside colloop_kernel)",
                     "ms": round(trail_ms, 4), "algorithmic_flops": far_flops,
                     "achieved": round(t_tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(t_tf / PEAK_BF16_TFLOPS, 4),
