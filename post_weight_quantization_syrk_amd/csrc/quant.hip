@@ -760,7 +760,7 @@ __global__ __launch_bounds__(256) void colloop_kernel(
 
 // Wc[:, n0:n1] -= delta[:, b0:b0+kb] * U[b0:b0+kb, n0:n1] on the bf16 matrix
 // cores.  Both operands come already split into their three bf16 parts (the
-// column loop splits the errors it writes, split_ut_kernel splits U^T once
+// column loop splits the errors it writes, uprep_kernel splits U^T once
 // per call), and the product is formed from the six part products that
 // matter,
 //   l*h + h*l + m*m + m*h + h*m + h*h,
@@ -770,10 +770,9 @@ __global__ __launch_bounds__(256) void colloop_kernel(
 // about one fp32 rounding, as with fp32 FMAs; the feedback is then as exact
 // as fp32 working weights allow.  TM x 64 tiles, K in chunks of 32 (two MFMA
 // steps of 16): a chunk of one part is one contiguous run of the k-chunk
-// major operands, loaded 16 bytes per lane.  Both LDS tiles are k-contiguous
-// rows (the error rows and the rows of U^T), so every lane reads its 8
-// consecutive k as 16 bytes; row pitches of 80 bytes keep those reads free of
-// bank conflicts.  The accumulators start at zero and collect delta U, and Wc
+// major operands, loaded 16 bytes per lane.  The LDS tile of U^T holds
+// k-contiguous rows, so every lane reads its 8 consecutive k as 16 bytes; a
+// row pitch of 80 bytes keeps those reads free of bank conflicts.  The accumulators start at zero and collect delta U, and Wc
 // - acc is stored: summed onto a preloaded Wc instead, every one of the K
 // roundings would be at the weights' magnitude rather than the products'.
 constexpr int T3K = KC;           // k per chunk
