@@ -925,10 +925,29 @@ __global__ __launch_bounds__(256) void inv_items_kernel(const float* __restrict_
 
 // U[i][j] = M[d-1-i][d-1-j] for i <= j, 0 below the diagonal.
 __global__ __launch_bounds__(256) void write_u_kernel(const float* __restrict__ M,
-                                                      float* __restrict__ U, int d) {
+                                                      float* __restrict__ U, int d, int vec) {
   const int64_t total = (int64_t)d * d;
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
-       e += (int64_t)gridDim.x * 256) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  if (vec) {
+    // four entries of a row per thread (d a multiple of 4, U 16-byte
+    // aligned): U[i][j .. j + 3] come from M[d - 1 - i][d - 4 - j .. d - 1 - j],
+    // one aligned float4 read backwards
+    for (int64_t e4 = (int64_t)blockIdx.x * 256 + threadIdx.x; e4 < total / 4; e4 += stride) {
+      const int64_t e = 4 * e4;
+      const int i = (int)(e / d), j = (int)(e % d);
+      float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j + 3 >= i) {
+        const float4 m = *(const float4*)(M + (int64_t)(d - 1 - i) * d + (d - 4 - j));
+        o.x = (i <= j) ? m.w : 0.0f;
+        o.y = (i <= j + 1) ? m.z : 0.0f;
+        o.z = (i <= j + 2) ? m.y : 0.0f;
+        o.w = m.x;
+      }
+      *(float4*)(U + e) = o;
+    }
+    return;
+  }
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += stride) {
     const int i = (int)(e / d), j = (int)(e % d);
     U[e] = (i <= j) ? M[(int64_t)(d - 1 - i) * d + (d - 1 - j)] : 0.0f;
   }
@@ -1015,8 +1034,10 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
     if (e != hipSuccess) return e;
   }
   const int64_t total = (int64_t)d * d;
-  const int grid = (int)std::min<int64_t>(ceil_div(total, 256), 65536);
-  hipLaunchKernelGGL(write_u_kernel, dim3(grid), dim3(256), 0, stream, (const float*)w.M, U, d);
+  const int vec = (d % 4 == 0) && ((uintptr_t)U % 16 == 0);
+  const int grid = (int)std::min<int64_t>(ceil_div(vec ? total / 4 : total, 256), 65536);
+  hipLaunchKernelGGL(write_u_kernel, dim3(grid), dim3(256), 0, stream, (const float*)w.M, U, d,
+                     vec);
   return hipGetLastError();
 }
 
