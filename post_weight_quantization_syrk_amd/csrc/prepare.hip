@@ -86,8 +86,12 @@ __device__ __forceinline__ void tri_coords(int t, int& ti, int& tj) {
 // dead[i] = (H_ii == 0); lambda = damp * mean(diag) with dead entries counted as 1.
 __global__ __launch_bounds__(1024) void prep_stats_kernel(const float* __restrict__ H, int d,
                                                           double damp, uint8_t* dead,
-                                                          double* scal, int32_t* status) {
+                                                          double* scal, int32_t* status,
+                                                          int* __restrict__ flags,
+                                                          int64_t nflags) {
   __shared__ double red[1024];
+  // the factorization's hand-off flags start at zero
+  for (int64_t i = threadIdx.x; i < nflags; i += 1024) flags[i] = 0;
   double s = 0.0;
   for (int i = threadIdx.x; i < d; i += 1024) {
     const float h = H[(int64_t)i * d + i];
@@ -475,11 +479,7 @@ __device__ __forceinline__ void diag_factor(DiagLds& L, float* __restrict__ A,
 // failed (dev_status set by another workgroup) or after `spin` polls, which
 // sets dev_status to SYNC_TIMEOUT; either way the workgroup leaves, so the
 // launch always drains.  Flags live in the workspace and are cleared before
-// the panels start.
-__global__ __launch_bounds__(256) void zero_ints_kernel(int* __restrict__ p, int64_t n) {
-  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
-    p[e] = 0;
-}
+// the panels start (by prep_stats_kernel, the first launch of the step).
 
 __device__ __forceinline__ void xstore2(float* p, float a, float b) {
   const uint64_t v = (uint64_t)__float_as_uint(a) | ((uint64_t)__float_as_uint(b) << 32);
@@ -981,8 +981,9 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
                                uint8_t* dead, int32_t* dev_status, void* ws, hipStream_t stream) {
   const int d = (int)d64;
   PrepWs w = carve(ws, d64);
+  const int64_t nflags = n_panels(d) * FLAGS_PER_PANEL;
   hipLaunchKernelGGL(prep_stats_kernel, dim3(1), dim3(1024), 0, stream, H, d, damp, dead, w.scal,
-                     dev_status);
+                     dev_status, w.flags, nflags);
   const int nt32 = (int)ceil_div(d, 32);
   hipLaunchKernelGGL(prep_build_kernel, dim3(nt32 * (nt32 + 1) / 2), dim3(256), 0, stream, H, d,
                      (const double*)w.scal, w.A);
@@ -990,9 +991,6 @@ hipError_t prepare_perm_launch(float* H, int64_t d64, double damp, const int32_t
     hipLaunchKernelGGL(prep_perm_kernel,
                        dim3((unsigned)ceil_div(d, 256), (unsigned)std::min(d, 1024)), dim3(256), 0,
                        stream, (const float*)H, d, perm, w.A);
-  const int64_t nflags = n_panels(d) * FLAGS_PER_PANEL;
-  hipLaunchKernelGGL(zero_ints_kernel, dim3((unsigned)ceil_div(nflags, 256)), dim3(256), 0,
-                     stream, w.flags, nflags);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t spin = sync_spin_limit();
