@@ -1038,10 +1038,41 @@ __global__ __launch_bounds__(256, (TM * TN >= 128 * 128) ? 2 : 1) void trailing3
 }
 
 // ---- pack -------------------------------------------------------------------
+// CPW > 0: bits divides 32, a row is a whole number of words (CPW = 32 /
+// bits codes each) and codes is aligned to CPW bytes, so word e holds codes
+// e CPW .. e CPW + CPW - 1 of the row-major matrix, read as one load.
+template <int CPW>
+__device__ __forceinline__ uint32_t pack_word(const uint8_t* __restrict__ codes, int64_t e) {
+  constexpr int B = 32 / CPW;
+  constexpr uint32_t MASK = (1u << B) - 1;
+  uint32_t b[CPW / 4];
+  if constexpr (CPW == 16) {
+    const uint4 v = *(const uint4*)(codes + 16 * e);
+    b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+  } else if constexpr (CPW == 8) {
+    const uint2 v = *(const uint2*)(codes + 8 * e);
+    b[0] = v.x; b[1] = v.y;
+  } else {
+    b[0] = *(const uint32_t*)(codes + 4 * e);
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int k = 0; k < CPW; ++k) acc |= ((b[k / 4] >> (8 * (k % 4))) & MASK) << (B * k);
+  return acc;
+}
+
 __global__ __launch_bounds__(256) void pack_codes_kernel(const uint8_t* __restrict__ codes,
                                                          int64_t d_out, int64_t d_in, int bits,
-                                                         int64_t words, uint32_t* __restrict__ qw) {
+                                                         int64_t words, uint32_t* __restrict__ qw,
+                                                         int cpw) {
   const int64_t total = d_out * words;
+  if (cpw) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * 256)
+      qw[e] = (cpw == 16) ? pack_word<16>(codes, e)
+              : (cpw == 8) ? pack_word<8>(codes, e) : pack_word<4>(codes, e);
+    return;
+  }
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
        e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / words, wi = e % words;
@@ -1237,10 +1268,13 @@ hipError_t pack_launch(const uint8_t* codes, const float* scales, const float* z
                        hipStream_t stream) {
   const int64_t words = ceil_div(d_in * bits, 32);
   const int64_t total = d_out * words;
+  const int cpw = (32 % bits == 0) ? 32 / bits : 0;
+  const int fast = (cpw >= 4 && cpw <= 16 && d_in % cpw == 0 && (uintptr_t)codes % cpw == 0)
+                       ? cpw : 0;
   if (total > 0)
     hipLaunchKernelGGL(pack_codes_kernel,
                        dim3((unsigned)std::min<int64_t>(ceil_div(total, 256), 65536)), dim3(256),
-                       0, stream, codes, d_out, d_in, bits, words, qweight);
+                       0, stream, codes, d_out, d_in, bits, words, qweight, fast);
   const int64_t nm = d_out * n_groups;
   if (nm > 0)
     hipLaunchKernelGGL(pack_meta_kernel,
